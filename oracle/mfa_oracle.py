@@ -1,0 +1,211 @@
+"""Plain float64 CPU definition of one MFA decode step (test infrastructure only).
+
+This module is the parity oracle. It is deliberately slow and literal: every
+step is the textbook definition written in numpy float64, one sequence at a
+time, with no tiling, no online softmax and no split/merge of the key range.
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use it; the
+HIP library never imports or calls it and it never calls the library.
+
+Sources (the text of the pages about "Step-3 is Large yet Affordable:
+Model-system Co-design for Cost-effective Decoding"):
+  * Step-3 paper summary (bud-325.pages.dev), "Key claims" and "Method": the
+    query is down-projected from hidden 7168 to rank 2048, normalized, and
+    up-projected to 64 heads of width 256; one K head and one V head of width
+    256 are shared by all 64 query heads; the cache holds one K and one V row
+    per token.
+  * redeep.blog Step3 post, "What's New" and the architecture table: the same
+    shapes (hidden 7168, 64 query heads, head size 256, query rank 2048).
+  * Step-3 paper index page (mlsanity.com), "Abstract": FP8 decoding.
+
+Readings where the pages are silent (each one is a choice this library makes):
+  * the normalization is RMSNorm, x * (mean(x^2) + eps)^-1/2 * gamma, eps 1e-6,
+    gamma defaulting to ones;
+  * softmax scale 1/sqrt(256) = 1/16; no rotary or other positional term;
+  * no projection biases; K and V are plain projections of the hidden state;
+  * weights are stored [out, in] (y = x W^T); column n of the up-projection is
+    head n // 256, channel n % 256, and the attention output is flattened the
+    same way before the out-projection;
+  * the single new query attends to every cached row of its sequence, the row
+    appended in this step included; no mask;
+  * log-sum-exp uses the natural log; a sequence with no rows gives output 0
+    and lse = -inf.
+
+Parity pins: every function here is checked against closed forms, hand-worked
+fixtures, invariants and a pure-Python brute force in tests/test_oracle_cpu.py.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+SOFTMAX_SCALE = 1.0 / math.sqrt(256.0)
+
+
+# ------------------------------------------------------------------ storage
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly.
+
+    A bfloat16 value is the upper 16 bits of an IEEE-754 binary32 word.
+    """
+    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return w.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_table() -> np.ndarray:
+    """The 256 values of the OCP FP8 E4M3 ("fn") format, indexed by byte.
+
+    Bit 7 is the sign, bits 6..3 the exponent (bias 7), bits 2..0 the mantissa.
+    Exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; there is
+    no infinity.
+    """
+    t = np.empty(256, dtype=np.float64)
+    for b in range(256):
+        sign = -1.0 if b & 0x80 else 1.0
+        e = (b >> 3) & 0xF
+        m = b & 0x7
+        if e == 0xF and m == 0x7:
+            t[b] = math.nan
+        elif e == 0:
+            t[b] = sign * math.ldexp(m, -9)
+        else:
+            t[b] = sign * math.ldexp(1.0 + m / 8.0, e - 7)
+    return t
+
+
+_E4M3 = e4m3fn_table()
+
+
+def decode_e4m3fn(codes: np.ndarray, scale) -> np.ndarray:
+    """fp8 bytes with a per-tensor float32 scale -> float64 (the product is exact)."""
+    return _E4M3[np.asarray(codes, dtype=np.uint8)] * np.float64(np.float32(scale))
+
+
+def to_f64(arr: np.ndarray, kind: str, scale=None) -> np.ndarray:
+    """Upcast a stored tensor ("f32", "bf16" bit patterns or "fp8_e4m3" bytes) to float64."""
+    if kind == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if kind == "bf16":
+        return decode_bf16(arr)
+    if kind == "fp8_e4m3":
+        return decode_e4m3fn(arr, scale)
+    raise ValueError(f"unknown storage kind {kind!r}")
+
+
+# ------------------------------------------------------------------ query path
+def rms_norm(c: np.ndarray, eps: float = 1e-6, gamma=None) -> np.ndarray:
+    """RMSNorm over the last axis: c / sqrt(mean(c^2) + eps) * gamma."""
+    c = np.asarray(c, dtype=np.float64)
+    ms = np.mean(c * c, axis=-1, keepdims=True)
+    out = c / np.sqrt(ms + eps)
+    if gamma is not None:
+        out = out * np.asarray(gamma, dtype=np.float64)
+    return out
+
+
+def q_path(x, w_dq, w_uq, eps=1e-6, gamma=None, n_heads=64, head_dim=256):
+    """Low-rank query: c = x W_dq^T, c_hat = RMSNorm(c), q = c_hat W_uq^T -> [B, H, D].
+
+    (Step-3 summary, "Method": down-projection 7168 -> 2048, normalization,
+    up-projection to 64 x 256.) Returns (c, c_hat, q).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    c = x @ np.asarray(w_dq, dtype=np.float64).T
+    c_hat = rms_norm(c, eps, gamma)
+    q = c_hat @ np.asarray(w_uq, dtype=np.float64).T
+    return c, c_hat, q.reshape(x.shape[0], n_heads, head_dim)
+
+
+def kv_project(x, w_k, w_v):
+    """The one shared K row and one shared V row of each new token: x W_k^T, x W_v^T.
+
+    (Step-3 summary, "Key claims"/"Method": a single K head and a single V head
+    of width 256 shared by all 64 query heads.)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x @ np.asarray(w_k, dtype=np.float64).T, x @ np.asarray(w_v, dtype=np.float64).T
+
+
+# ------------------------------------------------------------------ attention
+def attend_one(q_b, k_b, v_b, scale=SOFTMAX_SCALE):
+    """Softmax attention of H query rows over one shared K/V head.
+
+    S = q_b K_b^T * scale; m = row max; P = exp(S - m); l = row sum;
+    O = P V_b / l; lse = m + ln l. Two passes over the full row, no tiling.
+    With zero rows: O = 0 and lse = -inf.
+    """
+    q_b = np.asarray(q_b, dtype=np.float64)
+    k_b = np.asarray(k_b, dtype=np.float64)
+    v_b = np.asarray(v_b, dtype=np.float64)
+    H, D = q_b.shape
+    if k_b.shape[0] == 0:
+        return np.zeros((H, v_b.shape[1])), np.full(H, -np.inf)
+    s = (q_b @ k_b.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ v_b) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+def decode_attn(q, k_cache, v_cache, seq_off, seq_len, scale=SOFTMAX_SCALE,
+                kind_q="f64", kind_kv="f64", k_scale=None, v_scale=None, batch_ids=None):
+    """Attention for every sequence b over cache rows [off_b, off_b + len_b).
+
+    Inputs may be stored tensors (kind "f32" / "bf16" / "fp8_e4m3") or float64
+    ("f64"); each sequence is upcast separately to bound memory. ``batch_ids``
+    restricts the work to a subset of sequences (returned in that order).
+    Returns (O [n, H, D], lse [n, H]).
+    """
+    ids = range(len(seq_len)) if batch_ids is None else batch_ids
+
+    def up(a, kind, sc):
+        return np.asarray(a, dtype=np.float64) if kind == "f64" else to_f64(a, kind, sc)
+
+    outs, lses = [], []
+    for b in ids:
+        o0, n = int(seq_off[b]), int(seq_len[b])
+        qb = up(q[b], kind_q, None)
+        kb = up(k_cache[o0:o0 + n], kind_kv, k_scale)
+        vb = up(v_cache[o0:o0 + n], kind_kv, v_scale)
+        o, lse = attend_one(qb, kb, vb, scale)
+        outs.append(o)
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+# ------------------------------------------------------------------ output
+def out_proj(o, w_o):
+    """y = O_flat W_o^T with O flattened head-major ([B, H*D])."""
+    o = np.asarray(o, dtype=np.float64)
+    return o.reshape(o.shape[0], -1) @ np.asarray(w_o, dtype=np.float64).T
+
+
+# ------------------------------------------------------------------ whole step
+def decode_layer(inp: dict, batch_ids=None, scale=SOFTMAX_SCALE):
+    """One decode step of the attention layer from stored inputs.
+
+    q path -> K/V projection of the new token -> append at row off_b + len_b ->
+    attention over len_b + 1 rows -> out-projection. ``inp`` holds stored
+    tensors with their storage kinds (see the keys used below). Returns a dict
+    with c, c_hat, q, k_new, v_new, o, lse and y (float64); with ``batch_ids``
+    only those sequences are computed.
+    """
+    ka, kk = inp["kind_act"], inp["kind_kv"]
+    ids = list(range(len(inp["seq_len"]))) if batch_ids is None else list(batch_ids)
+    x = to_f64(inp["x"], ka)[ids]
+    w = {n: to_f64(inp[n], ka) for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o")}
+    c, c_hat, q = q_path(x, w["w_dq"], w["w_uq"], inp.get("eps", 1e-6), inp.get("gamma"))
+    k_new, v_new = kv_project(x, w["w_k"], w["w_v"])
+    outs, lses = [], []
+    for i, b in enumerate(ids):
+        o0, n = int(inp["seq_off"][b]), int(inp["seq_len"][b])
+        kb = np.concatenate([to_f64(inp["k_cache"][o0:o0 + n], kk), k_new[i:i + 1]])
+        vb = np.concatenate([to_f64(inp["v_cache"][o0:o0 + n], kk), v_new[i:i + 1]])
+        o, lse = attend_one(q[i], kb, vb, scale)
+        outs.append(o)
+        lses.append(lse)
+    o = np.stack(outs)
+    y = out_proj(o, w["w_o"])
+    return dict(c=c, c_hat=c_hat, q=q, k_new=k_new, v_new=v_new, o=o, lse=np.stack(lses), y=y)

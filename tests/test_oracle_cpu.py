@@ -1,0 +1,379 @@
+"""Pins for the CPU oracle (no GPU).
+
+Every check here ties the oracle to something other than itself: fixtures
+worked by hand from a format or closed form (tests/golden), invariants the
+definition implies, and a pure-Python brute force that treats the shared K/V
+head as 64 replicated heads. Each is chosen so that a plausible slip (a dropped
+scale, a wrong sign, a transposed operand, a wrong head order, eps outside the
+square root, a missing max subtraction, an unread appended row) fails.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from conftest import read_golden
+from decode_attention_attn_amd import inputs as gen
+from oracle import brute
+from oracle import mfa_oracle as om
+
+
+# ------------------------------------------------------------------ storage codecs
+def test_bf16_decode_matches_format_fixture():
+    for bits, val in read_golden("bf16_points.txt"):
+        got = om.decode_bf16(np.array([int(bits, 16)], dtype=np.uint16))[0]
+        want = float(val)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (bits, got, want)
+
+
+def test_e4m3fn_decode_matches_spec_fixture():
+    t = om.e4m3fn_table()
+    for byte, val in read_golden("e4m3fn_points.txt"):
+        got = t[int(byte, 16)]
+        if val == "nan":
+            assert math.isnan(got), byte
+        else:
+            want = float(val)
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (byte, got, want)
+
+
+def test_e4m3fn_table_structure():
+    t = om.e4m3fn_table()
+    nans = [b for b in range(256) if math.isnan(t[b])]
+    assert nans == [0x7F, 0xFF]
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)  # codes are ordered by magnitude
+    for b in range(0x7F):
+        assert t[b | 0x80] == -t[b]
+    # within one binade the 8 codes are evenly spaced, and the spacing doubles per binade
+    for e in range(1, 15):
+        step = np.diff(t[e * 8: e * 8 + 8])
+        assert np.all(step == 2.0 ** (e - 10))
+    assert np.all(np.diff(t[0:8]) == 2.0 ** -9)  # subnormals continue the first binade's step
+
+
+def test_decode_e4m3fn_scale_product_is_exact():
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    s = np.float32(6.0 / 448.0)
+    got = om.decode_e4m3fn(codes, s)
+    want = np.array([float(om.e4m3fn_table()[c]) * float(s) for c in codes])
+    assert np.array_equal(got, want)
+
+
+def test_generator_bf16_rounding_fixture():
+    for val, bits in read_golden("bf16_rounding.txt"):
+        got = gen.f32_to_bf16_bits(np.array([float(val)], dtype=np.float32))[0]
+        assert int(got) == int(bits, 16), (val, hex(got), bits)
+
+
+def test_generator_e4m3_encoder_against_oracle_decoder():
+    # Two independent implementations of one format: every finite code round-trips.
+    t = om.e4m3fn_table()
+    finite = [b for b in range(256) if not math.isnan(t[b])]
+    codes = gen.encode_e4m3fn(t[finite])
+    for b, c in zip(finite, codes):
+        if b == 0x80:
+            assert c in (0x00, 0x80)
+        else:
+            assert int(c) == b
+    # exact midpoints round to the even code; beyond 448 saturates
+    mids = (t[0x38] + t[0x39]) / 2, (t[0x39] + t[0x3A]) / 2
+    assert list(gen.encode_e4m3fn(np.array(mids))) == [0x38, 0x3A]
+    assert list(gen.encode_e4m3fn(np.array([1e4, -1e4, 449.0]))) == [0x7E, 0xFE, 0x7E]
+    # every value quantizes to its nearest code
+    rng = np.random.default_rng(5)
+    v = rng.uniform(-448, 448, 2000)
+    codes = gen.encode_e4m3fn(v)
+    err = np.abs(t[codes] - v)
+    best = np.min(np.abs(t[np.isfinite(t)][None, :] - v[:, None]), axis=1)
+    assert np.all(err == best)
+
+
+# ------------------------------------------------------------------ attention
+def _two_rows():
+    g = {r[0]: [float(x) for x in r[1:]] for r in read_golden("attn_two_rows.txt")}
+    return g
+
+
+def test_attention_two_rows_fixture():
+    g = _two_rows()
+    q = np.array([g["q"]])
+    k = np.array([g["k1"], g["k2"]])
+    v = np.array([g["v1"], g["v2"]])
+    o, lse = om.attend_one(q, k, v, scale=1.0 / 16)
+    assert np.allclose(o[0], g["o"], rtol=0, atol=1e-12)
+    assert abs(lse[0] - g["lse"][0]) < 1e-12
+    bo, bl = brute.mha([g["q"]], [k.tolist()], [v.tolist()], 1.0 / 16)
+    assert np.allclose(bo[0], g["o"], atol=1e-12) and abs(bl[0] - g["lse"][0]) < 1e-12
+
+
+def test_default_scale_is_one_over_sqrt_head_dim():
+    assert om.SOFTMAX_SCALE == 0.0625
+
+
+def test_length_one_returns_v_exactly():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((64, 256))
+    k = rng.standard_normal((1, 256))
+    v = rng.standard_normal((1, 256))
+    o, lse = om.attend_one(q, k, v)
+    assert np.array_equal(o, np.repeat(v, 64, axis=0))
+    assert np.allclose(lse, (q @ k[0]) / 16, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["const_k", "zero_q"])
+def test_uniform_scores_give_mean_of_v(mode):
+    rng = np.random.default_rng(2)
+    L = 37
+    q = rng.standard_normal((64, 256))
+    k = np.repeat(rng.standard_normal((1, 256)), L, axis=0) if mode == "const_k" else rng.standard_normal((L, 256))
+    if mode == "zero_q":
+        q[:] = 0
+    v = rng.standard_normal((L, 256))
+    o, _ = om.attend_one(q, k, v)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-12)
+
+
+def test_weights_sum_to_one_and_match_closed_form():
+    rng = np.random.default_rng(3)
+    L = 9
+    q = rng.standard_normal((4, 16))
+    k = rng.standard_normal((L, 16))
+    o, lse = om.attend_one(q, k, np.ones((L, 16)), scale=0.25)
+    assert np.allclose(o, 1.0, atol=1e-14)
+    # V = identity turns the output into the weight matrix itself
+    w, _ = om.attend_one(q, k, np.eye(L), scale=0.25)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-14)
+    for h in range(4):
+        s = [float(q[h] @ k[j]) * 0.25 for j in range(L)]
+        z = math.fsum(math.exp(x) for x in s)
+        assert np.allclose(w[h], [math.exp(x) / z for x in s], atol=1e-14)
+        assert abs(lse[h] - math.log(z)) < 1e-12
+
+
+@pytest.mark.parametrize("H,D,L", [(4, 8, 1), (4, 8, 9), (64, 8, 5), (4, 256, 7), (64, 256, 3)])
+def test_matches_bruteforce_mha_with_replicated_kv(H, D, L):
+    rng = np.random.default_rng(H * 1000 + D * 10 + L)
+    B = 2
+    q = rng.standard_normal((B, H, D))
+    lens = np.array([L, max(L - 2, 1)], dtype=np.int32)
+    off = np.array([0, L], dtype=np.int64)
+    kc = rng.standard_normal((2 * L, D)) * 2.0
+    vc = rng.standard_normal((2 * L, D))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = om.decode_attn(q, kc, vc, off, lens, scale=scale)
+    for b in range(B):
+        rows_k = kc[off[b]: off[b] + lens[b]].tolist()
+        rows_v = vc[off[b]: off[b] + lens[b]].tolist()
+        bo, bl = brute.mha(q[b].tolist(), [rows_k] * H, [rows_v] * H, scale)
+        assert np.allclose(o[b], bo, rtol=0, atol=1e-12)
+        assert np.allclose(lse[b], bl, rtol=0, atol=1e-12)
+
+
+def test_permuting_cache_rows_leaves_output_unchanged():
+    rng = np.random.default_rng(4)
+    L = 50
+    q, k, v = rng.standard_normal((64, 256)), rng.standard_normal((L, 256)), rng.standard_normal((L, 256))
+    p = rng.permutation(L)
+    o1, l1 = om.attend_one(q, k, v)
+    o2, l2 = om.attend_one(q, k[p], v[p])
+    assert np.allclose(o1, o2, atol=1e-13) and np.allclose(l1, l2, atol=1e-12)
+
+
+def test_large_score_shift_is_stable():
+    # K -> K + 1 c^T shifts every score of head h by (q_h . c)/16, ~1e3 here;
+    # exp would overflow without the max subtraction.
+    rng = np.random.default_rng(5)
+    L = 40
+    q, k, v = rng.standard_normal((64, 256)), rng.standard_normal((L, 256)), rng.standard_normal((L, 256))
+    c = q.sum(axis=0)
+    c = c / np.linalg.norm(c) * 1000.0
+    o1, l1 = om.attend_one(q, k, v)
+    o2, l2 = om.attend_one(q, k + c, v)
+    assert np.all(np.isfinite(o2))
+    assert np.allclose(o1, o2, atol=1e-9)
+    assert np.allclose(l2 - l1, (q @ c) / 16, atol=1e-8)
+
+
+def test_affine_map_of_v_passes_through():
+    rng = np.random.default_rng(6)
+    L = 21
+    q, k, v = rng.standard_normal((8, 32)), rng.standard_normal((L, 32)), rng.standard_normal((L, 32))
+    A = rng.standard_normal((32, 32))
+    bvec = rng.standard_normal(32)
+    o1, _ = om.attend_one(q, k, v, scale=0.2)
+    o2, _ = om.attend_one(q, k, v @ A + bvec, scale=0.2)
+    assert np.allclose(o2, o1 @ A + bvec, atol=1e-11)
+
+
+def test_any_partition_merges_back_by_lse():
+    rng = np.random.default_rng(7)
+    L = 100
+    q, k, v = rng.standard_normal((64, 256)), rng.standard_normal((L, 256)), rng.standard_normal((L, 256))
+    o, lse = om.attend_one(q, k, v)
+    cuts = [0, 13, 13, 60, 99, 100]  # includes an empty part
+    parts = [om.attend_one(q, k[a:b], v[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
+    lses = np.stack([p[1] for p in parts])
+    m = lses.max(axis=0)
+    wts = np.exp(lses - m)
+    merged = sum(wts[i][:, None] * parts[i][0] for i in range(len(parts))) / wts.sum(axis=0)[:, None]
+    assert np.allclose(merged, o, atol=1e-13)
+    assert np.allclose(m + np.log(wts.sum(axis=0)), lse, atol=1e-12)
+
+
+def test_empty_sequence_gives_zero_and_minus_inf():
+    o, lse = om.attend_one(np.ones((64, 256)), np.zeros((0, 256)), np.zeros((0, 256)))
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_decode_attn_slices_each_sequence_and_decodes_storage():
+    w = gen.scaled(gen.WORKLOADS["attn_fp8kv_4k"], batch=3, ctx=0)
+    lens = np.array([5, 0, 17], dtype=np.int32)
+    inp = gen.make_attn(w, lengths=lens)
+    o, lse = om.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_off"], lens,
+                            kind_q="bf16", kind_kv="fp8_e4m3", k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    q2 = om.decode_bf16(inp["q"][2])
+    k2 = om.decode_e4m3fn(inp["k_cache"][5:22], inp["k_scale"])
+    v2 = om.decode_e4m3fn(inp["v_cache"][5:22], inp["v_scale"])
+    bo, bl = brute.mha(q2.tolist(), [k2.tolist()] * 64, [v2.tolist()] * 64, 1 / 16)
+    assert np.allclose(o[2], bo, atol=1e-12) and np.allclose(lse[2], bl, atol=1e-12)
+
+
+# ------------------------------------------------------------------ query path
+def test_rmsnorm_closed_forms():
+    eps = 1e-6
+    # constant vector a*1: c_hat = a / sqrt(a^2 + eps); eps matters at a = 1e-3
+    for a in (1e-3, 0.5, -2.0):
+        got = om.rms_norm(np.full((1, 2048), a), eps)
+        assert np.allclose(got, a / math.sqrt(a * a + eps), rtol=1e-14)
+    assert abs(om.rms_norm(np.full((1, 8), 1e-3), eps)[0, 0] - 1 / math.sqrt(2)) < 1e-12
+    got = om.rms_norm(np.array([[3.0, 4.0]]), eps)
+    assert np.allclose(got, np.array([[3.0, 4.0]]) / math.sqrt(12.5 + eps), rtol=1e-14)
+    rng = np.random.default_rng(8)
+    c = rng.standard_normal((3, 2048))
+    ms = np.mean(c * c, axis=1)
+    chat = om.rms_norm(c, eps)
+    assert np.allclose(np.mean(chat * chat, axis=1), ms / (ms + eps), rtol=1e-12)
+    assert np.allclose(om.rms_norm(7.5 * c, 0.0), om.rms_norm(c, 0.0), rtol=1e-12)
+    g = rng.standard_normal(2048)
+    assert np.allclose(om.rms_norm(c, eps, g), om.rms_norm(c, eps) * g, rtol=1e-14)
+    assert np.allclose([brute.rms_norm(c[0].tolist(), eps)], chat[:1], rtol=1e-13)
+
+
+def test_q_path_small_against_bruteforce():
+    rng = np.random.default_rng(9)
+    B, hid, r, H, D = 2, 48, 12, 4, 6
+    x = rng.standard_normal((B, hid))
+    wdq = rng.standard_normal((r, hid)) / math.sqrt(hid)
+    wuq = rng.standard_normal((H * D, r)) / math.sqrt(r)
+    c, chat, q = om.q_path(x, wdq, wuq, 1e-6, None, H, D)
+    for b in range(B):
+        cb = brute.matvec_t(x[b].tolist(), wdq.tolist())
+        ch = brute.rms_norm(cb, 1e-6)
+        qb = brute.matvec_t(ch, wuq.tolist())
+        assert np.allclose(c[b], cb, atol=1e-13)
+        for h in range(H):
+            assert np.allclose(q[b, h], qb[h * D:(h + 1) * D], atol=1e-13)
+
+
+def test_q_path_head_major_layout():
+    # one-hot up-projection: row n of W_uq picks channel n % r of c_hat,
+    # so q[b, h, d] must be c_hat[b, (h*D + d) % r]
+    rng = np.random.default_rng(10)
+    B, hid, r, H, D = 2, 20, 10, 3, 4
+    x = rng.standard_normal((B, hid))
+    wdq = rng.standard_normal((r, hid))
+    wuq = np.zeros((H * D, r))
+    for n in range(H * D):
+        wuq[n, n % r] = 1.0
+    _, chat, q = om.q_path(x, wdq, wuq, 1e-6, None, H, D)
+    for h in range(H):
+        for d in range(D):
+            assert q[0, h, d] == chat[0, (h * D + d) % r]
+
+
+def test_out_proj_flattens_head_major():
+    rng = np.random.default_rng(11)
+    B, H, D, N = 2, 3, 4, 5
+    o = rng.standard_normal((B, H, D))
+    pick = [7, 0, 11, 4, 9]  # y[:, j] = o_flat[:, pick[j]], o_flat[h*D + d] = o[h, d]
+    wo = np.zeros((N, H * D))
+    for j, p in enumerate(pick):
+        wo[j, p] = 1.0
+    y = om.out_proj(o, wo)
+    for j, p in enumerate(pick):
+        assert np.array_equal(y[:, j], o[:, p // D, p % D])
+
+
+def test_layer_full_size_spot_checks_against_fsum():
+    # Real shapes (tiny_fp32 workload): spot-check numpy's float64 GEMMs against
+    # correctly rounded sums of exactly representable products.
+    inp = gen.make_layer(gen.WORKLOADS["tiny_fp32"])
+    out = om.decode_layer(inp)
+    x = inp["x"].astype(np.float64)
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        b = int(rng.integers(2))
+        n = int(rng.integers(2048))
+        want = math.fsum((x[b] * inp["w_dq"][n].astype(np.float64)).tolist())
+        assert abs(out["c"][b, n] - want) <= 1e-12 * (1 + abs(want))
+        j = int(rng.integers(16384))
+        want = math.fsum((out["c_hat"][b] * inp["w_uq"][j].astype(np.float64)).tolist())
+        assert abs(out["q"][b, j // 256, j % 256] - want) <= 1e-12 * (1 + abs(want))
+        j = int(rng.integers(256))
+        want = math.fsum((x[b] * inp["w_k"][j].astype(np.float64)).tolist())
+        assert abs(out["k_new"][b, j] - want) <= 1e-12 * (1 + abs(want))
+        want = math.fsum((x[b] * inp["w_v"][j].astype(np.float64)).tolist())
+        assert abs(out["v_new"][b, j] - want) <= 1e-12 * (1 + abs(want))
+        j = int(rng.integers(7168))
+        want = math.fsum((out["o"][b].reshape(-1) * inp["w_o"][j].astype(np.float64)).tolist())
+        assert abs(out["y"][b, j] - want) <= 1e-12 * (1 + abs(want))
+    assert out["o"].shape == (2, 64, 256) and out["y"].shape == (2, 7168)
+
+
+def _small_layer(seed=13, B=3, ctx=6):
+    rng = np.random.default_rng(seed)
+    hid, r = 7168, 2048
+    cap = ctx + 2
+    inp = dict(
+        kind_act="f32", kind_kv="f32", eps=1e-6,
+        x=rng.standard_normal((B, hid)).astype(np.float32),
+        w_dq=(rng.standard_normal((r, hid)) / math.sqrt(hid)).astype(np.float32),
+        w_uq=(rng.standard_normal((16384, r)) / math.sqrt(r)).astype(np.float32),
+        w_k=(rng.standard_normal((256, hid)) / math.sqrt(hid)).astype(np.float32),
+        w_v=(rng.standard_normal((256, hid)) / math.sqrt(hid)).astype(np.float32),
+        w_o=(rng.standard_normal((7168, 16384)) / 128).astype(np.float32),
+        k_cache=rng.standard_normal((B * cap, 256)).astype(np.float32),
+        v_cache=rng.standard_normal((B * cap, 256)).astype(np.float32),
+        seq_off=np.arange(B, dtype=np.int64) * cap,
+        seq_len=np.full(B, ctx, dtype=np.int32),
+    )
+    return inp
+
+
+def test_layer_attends_the_appended_row_and_nothing_beyond():
+    inp = _small_layer()
+    out = om.decode_layer(inp)
+    # with zero K/V projections the appended row has k = 0, v = 0: score 0,
+    # so lse' = logaddexp(lse, 0) and o' = o * exp(lse - lse') over the cached rows
+    z = dict(inp, w_k=np.zeros_like(inp["w_k"]), w_v=np.zeros_like(inp["w_v"]))
+    outz = om.decode_layer(z)
+    for b in range(3):
+        o0, n = int(inp["seq_off"][b]), int(inp["seq_len"][b])
+        oc, lc = om.attend_one(outz["q"][b], inp["k_cache"][o0:o0 + n], inp["v_cache"][o0:o0 + n])
+        ln = np.logaddexp(lc, 0.0)
+        assert np.allclose(outz["lse"][b], ln, atol=1e-12)
+        assert np.allclose(outz["o"][b], oc * np.exp(lc - ln)[:, None], atol=1e-12)
+    # rows past len (the free slot and beyond) are never read
+    poisoned = dict(inp, k_cache=inp["k_cache"].copy(), v_cache=inp["v_cache"].copy())
+    for b in range(3):
+        o0, n = int(inp["seq_off"][b]), int(inp["seq_len"][b])
+        poisoned["k_cache"][o0 + n:o0 + n + 2] = 1e30
+        poisoned["v_cache"][o0 + n:o0 + n + 2] = np.nan
+    outp = om.decode_layer(poisoned)
+    assert np.array_equal(outp["o"], out["o"]) and np.array_equal(outp["y"], out["y"])
+    # a single sequence computed alone equals its row of the batch
+    one = om.decode_layer(inp, batch_ids=[2])
+    assert np.allclose(one["y"][0], out["y"][2], atol=1e-12)
