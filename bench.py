@@ -1,0 +1,220 @@
+"""Benchmark of the MFA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the measured path over one batch of synthetic input
+already resident in HBM:
+  * attention workloads (default ``attn_bf16_4k``: batch 32, 64 query heads
+    over one shared bf16 K/V head, 4096 positions): one ``mfa_decode_attn``
+    call, i.e. scores, online softmax, PV and the split merge;
+  * ``layer_bf16_8k`` / ``tiny_fp32``: the whole decode layer (q path, K/V
+    append, attention, out-projection).
+Prints one JSON line. ``value`` is KV-cache bytes read per second (GB/s) over
+the whole step; ``tokens_per_s`` is sequences decoded per second for this one
+layer. The K/V buffers rotate over several copies so that the 256 MB on-die
+cache cannot serve a repeated working set. The CPU oracle is timed on a
+bounded sample of the same workload on the host cores (``cpu_baseline``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MFA decode attn: KV-cache HBM GB/s (% of peak) + decode tokens/s at 4K ctx"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def _kv_bytes(lengths, kv_kind):
+    import numpy as np
+
+    per = 512 * (1 if kv_kind == "fp8_e4m3" else (4 if kv_kind == "f32" else 2))
+    return int(np.asarray(lengths, dtype=np.int64).sum()) * per
+
+
+def _event_time_ms(fn, steps, warmup, stream):
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_attn(name, steps, warmup, rotate):
+    import torch
+
+    from decode_attention_attn_amd import inputs as gen
+    from decode_attention_attn_amd import runner
+
+    w = gen.WORKLOADS[name]
+    inp = gen.make_attn(w)
+    dev = runner.upload_attn(inp)
+    ks = [dev["k"]] + [dev["k"].clone() for _ in range(rotate - 1)]
+    vs = [dev["v"]] + [dev["v"].clone() for _ in range(rotate - 1)]
+    stream = torch.cuda.current_stream()
+    call = runner.AttnCall(dev, num_workgroups=0, want_lse=False, stream=stream.cuda_stream)
+    ms = _event_time_ms(lambda i: call(ks[i % rotate], vs[i % rotate]), steps, warmup, stream)
+    B = w.batch
+    kv = _kv_bytes(inp["seq_len"], w.kv)
+    qo = 2 * B * 64 * 256 * (4 if w.act == "f32" else 2)
+    return dict(workload=name, ms=ms, B=B, kv_bytes=kv, alg_bytes=kv + qo, lengths=inp["seq_len"], inp=inp, w=w)
+
+
+def bench_layer(name, steps, warmup):
+    import torch
+
+    from decode_attention_attn_amd import inputs as gen
+    from decode_attention_attn_amd import runner
+
+    w = gen.WORKLOADS[name]
+    inp = gen.make_layer(w)
+    dev = runner.upload_layer(inp)
+    stream = torch.cuda.current_stream()
+    call = runner.LayerCall(dev, num_workgroups=0, stream=stream.cuda_stream)
+    ms = _event_time_ms(lambda i: call(), steps, warmup, stream)
+    B = w.batch
+    esz = 4 if w.act == "f32" else 2
+    kv = _kv_bytes(inp["seq_len"] + 1, w.kv)
+    weights = (2048 * 7168 + 16384 * 2048 + 2 * 256 * 7168 + 7168 * 16384) * esz
+    return dict(workload=name, ms=ms, B=B, kv_bytes=kv, alg_bytes=kv + weights, lengths=inp["seq_len"] + 1,
+                inp=inp, w=w)
+
+
+def cpu_baseline(res, seconds):
+    """Time the float64 oracle on the host for about ``seconds`` on a sample of the workload."""
+    import numpy as np
+
+    from oracle import mfa_oracle as om
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp, w = res["inp"], res["w"]
+    B = len(inp["seq_len"])
+    done_seqs, done_kv, t0 = 0, 0, time.perf_counter()
+    b = 0
+    while time.perf_counter() - t0 < seconds:
+        if w.kind == "attn":
+            om.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_off"], inp["seq_len"],
+                           kind_q=inp["kind_q"], kind_kv=inp["kind_kv"], k_scale=inp["k_scale"],
+                           v_scale=inp["v_scale"], batch_ids=[b])
+            done_kv += _kv_bytes([inp["seq_len"][b]], w.kv)
+        else:
+            om.decode_layer(inp, batch_ids=[b])
+            done_kv += _kv_bytes([inp["seq_len"][b] + 1], w.kv)
+        done_seqs += 1
+        b = (b + 1) % B
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done_kv / dt / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(done_seqs / dt, 3),
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done_seqs} sequences of {w.name} (cycling over the batch), {dt:.1f} s, numpy float64",
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="attn_bf16_4k",
+                    choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "layer_bf16_8k", "tiny_fp32"])
+    ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the fp8-KV 4K secondary measurement")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import decode_attention_attn_amd.mfa  # noqa: F401  (fails loudly if libmfa.so is missing)
+
+    if args.workload.startswith("attn"):
+        res = bench_attn(args.workload, args.steps, args.warmup, args.rotate)
+    else:
+        res = bench_layer(args.workload, args.steps, args.warmup)
+    w = res["w"]
+    ms = res["ms"]
+    gbps = res["kv_bytes"] / (ms * 1e-3) / 1e9
+    achieved = res["alg_bytes"] / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "ctx": int(max(res["lengths"])),
+            "q_heads": 64,
+            "kv_heads": 1,
+            "head_dim": 256,
+            "kv_dtype": w.kv,
+            "kv_buffer_sets": args.rotate if w.kind == "attn" else 1,
+        },
+        "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "pct_of_peak_hbm": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "attn_mfma_kernel + attn_combine_kernel (whole call, HIP events)"
+            if w.kind == "attn" else "whole layer (HIP events)",
+            "alg_bytes_per_launch": res["alg_bytes"],
+        },
+    }
+    if w.kind == "attn" and not args.no_secondary and args.workload == "attn_bf16_4k":
+        sec = bench_attn("attn_fp8kv_4k", args.steps, args.warmup, args.rotate)
+        s_gbps = sec["kv_bytes"] / (sec["ms"] * 1e-3) / 1e9
+        line["secondary"] = {"attn_fp8kv_4k": {
+            "ms_per_step": round(sec["ms"], 5), "kv_GBps": round(s_gbps, 2),
+            "pct_of_peak_hbm": round(100 * s_gbps / HBM_PEAK_GBPS, 2),
+            "tokens_per_s": round(sec["B"] / (sec["ms"] * 1e-3), 1)}}
+        del sec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+// C ABI of libmfa: argument validation, workspace sizing and dispatch to the
+// HIP kernels. Every check that can be made on the host runs before the first
+// HIP call, so invalid calls fail the same way on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <atomic>
+
+#include "../../include/mfa.h"
+#include "mfa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned_n(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
+// Compute units of the current device (cached per device).
+int current_cu_count(int* status) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *status = MFA_ERR_HIP;
+    return 0;
+  }
+  if (dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    *status = MFA_ERR_HIP;
+    return 0;
+  }
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool act_dtype_ok(mfa_dtype dt) { return dt == MFA_F32 || dt == MFA_BF16; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// HIP failures map to MFA_ERR_HIP; with MFA_DEBUG set the HIP error is printed.
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MFA_OK;
+  if (getenv("MFA_DEBUG")) fprintf(stderr, "libmfa: HIP error %d: %s\n", (int)e, hipGetErrorString(e));
+  return MFA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mfa_version(void) { return 10000 * 1 + 100 * 0 + 0; }
+
+const char* mfa_status_string(int status) {
+  switch (status) {
+    case MFA_OK: return "MFA_OK";
+    case MFA_ERR_INVALID_ARG: return "MFA_ERR_INVALID_ARG: null pointer or size out of range";
+    case MFA_ERR_UNSUPPORTED: return "MFA_ERR_UNSUPPORTED: dtype combination not provided";
+    case MFA_ERR_ALIGNMENT: return "MFA_ERR_ALIGNMENT: pointer not suitably aligned";
+    case MFA_ERR_WORKSPACE: return "MFA_ERR_WORKSPACE: workspace missing or too small";
+    case MFA_ERR_HIP: return "MFA_ERR_HIP: HIP runtime call or kernel launch failed";
+    default: return "unknown libmfa status";
+  }
+}
+
+// ------------------------------------------------------------------ q path
+static size_t qproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* plan_out) {
+  const bool bf = dt == MFA_BF16;
+  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK);
+  if (plan_out) *plan_out = p;
+  const size_t part = bf ? mfa::gemm_partial_bytes(p) : (size_t)B * MFA_RANK * sizeof(float);
+  const size_t chat = (size_t)B * MFA_RANK * (bf ? 2 : 4);
+  return align256(part) + align256(chat);
+}
+
+size_t mfa_qproj_workspace_size(int B, mfa_dtype dt) {
+  if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(dt)) return 0;
+  return qproj_ws(B, dt, nullptr);
+}
+
+int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq, void* q_out, void* ws,
+              size_t ws_bytes, int B, mfa_dtype dt, void* stream) {
+  if (!x || !w_dq || !w_uq || !q_out || B < 1 || B > MFA_MAX_BATCH || !(eps >= 0.f) || !isfinite(eps))
+    return MFA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(dt)) return MFA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(q_out) || !aligned16(ws) ||
+      (gamma && !aligned_n(gamma, 4)))
+    return MFA_ERR_ALIGNMENT;
+  mfa::GemmPlan plan;
+  const size_t need = qproj_ws(B, dt, &plan);
+  if (!ws || ws_bytes < need) return MFA_ERR_WORKSPACE;
+  const bool bf = dt == MFA_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  float* part = (float*)ws;
+  void* chat = (char*)ws + align256(bf ? mfa::gemm_partial_bytes(plan) : (size_t)B * MFA_RANK * sizeof(float));
+  hipError_t e = mfa::launch_gemm(bf, plan, x, w_dq, w_dq, part, mfa::GemmOut::Partial, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = mfa::launch_rmsnorm_reduce(bf, part, bf ? plan.splits : 1, B, MFA_RANK, gamma, eps, chat, s);
+  if (e != hipSuccess) return hip_status(e);
+  const mfa::GemmPlan up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM);
+  if (bf && up.splits != 1) {
+    // the up-projection has 128 column tiles per 128 rows: never split
+    return MFA_ERR_HIP;
+  }
+  e = mfa::launch_gemm(bf, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s);
+  return hip_status(e);
+}
+
+// ------------------------------------------------------------------ K/V append
+static size_t kv_ws(int B, mfa_dtype act_dt, mfa::GemmPlan* plan_out) {
+  const bool bf = act_dt == MFA_BF16;
+  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM);
+  if (plan_out) *plan_out = p;
+  return align256(bf ? mfa::gemm_partial_bytes(p) : (size_t)B * 2 * MFA_HEAD_DIM * sizeof(float));
+}
+
+size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt) {
+  if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(act_dt)) return 0;
+  return kv_ws(B, act_dt, nullptr);
+}
+
+int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
+                  const int64_t* seq_off, const int32_t* seq_len, void* ws, size_t ws_bytes, int B, mfa_dtype act_dt,
+                  mfa_dtype cache_dt, void* stream) {
+  if (!x || !w_k || !w_v || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 || B > MFA_MAX_BATCH)
+    return MFA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(act_dt) || cache_dt != act_dt) return MFA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
+    return MFA_ERR_ALIGNMENT;
+  mfa::GemmPlan plan;
+  const size_t need = kv_ws(B, act_dt, &plan);
+  if (!ws || ws_bytes < need) return MFA_ERR_WORKSPACE;
+  const bool bf = act_dt == MFA_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = mfa::launch_kv_scatter(bf, (const float*)ws, bf ? plan.splits : 1, B, k_cache, v_cache, seq_off, seq_len, s);
+  return hip_status(e);
+}
+
+// ------------------------------------------------------------------ attention
+size_t mfa_decode_attn_workspace_size(int B, int num_workgroups) {
+  if (B < 1 || B > MFA_MAX_BATCH || num_workgroups < 0 || num_workgroups > 65536) return 0;
+  int G = num_workgroups;
+  if (G == 0) {
+    int st = MFA_OK;
+    G = current_cu_count(&st);
+    if (st != MFA_OK) return 0;
+  }
+  return mfa::attn_ws_bytes(B, G);
+}
+
+int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                    const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale, void* out, float* lse,
+                    void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
+                    void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_off || !seq_len || !out || B < 1 || B > MFA_MAX_BATCH ||
+      num_workgroups < 0 || num_workgroups > 65536 || !isfinite(softmax_scale) || !isfinite(k_scale) ||
+      !isfinite(v_scale))
+    return MFA_ERR_INVALID_ARG;
+  mfa::AttnKind kind;
+  if (q_dt == MFA_F32 && kv_dt == MFA_F32)
+    kind = mfa::AttnKind::F32;
+  else if (q_dt == MFA_BF16 && kv_dt == MFA_BF16)
+    kind = mfa::AttnKind::BF16;
+  else if (q_dt == MFA_BF16 && kv_dt == MFA_FP8_E4M3)
+    kind = mfa::AttnKind::BF16_FP8KV;
+  else
+    return MFA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws) ||
+      !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) || (lse && !aligned_n(lse, 4)))
+    return MFA_ERR_ALIGNMENT;
+  if (!ws) return MFA_ERR_WORKSPACE;
+  int G = num_workgroups;
+  if (G == 0) {
+    int st = MFA_OK;
+    G = current_cu_count(&st);
+    if (st != MFA_OK) return st;
+  }
+  if (ws_bytes < mfa::attn_ws_bytes(B, G)) return MFA_ERR_WORKSPACE;
+  mfa::AttnLaunch p;
+  p.kind = kind;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.seq_off = seq_off;
+  p.seq_len = seq_len;
+  p.out = out;
+  p.lse = lse;
+  p.ws = ws;
+  p.B = B;
+  p.G = G;
+  p.softmax_scale = softmax_scale;
+  p.k_scale = kind == mfa::AttnKind::BF16_FP8KV ? k_scale : 1.f;
+  p.v_scale = kind == mfa::AttnKind::BF16_FP8KV ? v_scale : 1.f;
+  return hip_status(mfa::launch_decode_attn(p, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ out-projection
+static size_t oproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* plan_out) {
+  const bool bf = dt == MFA_BF16;
+  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN);
+  if (plan_out) *plan_out = p;
+  return (bf && p.splits > 1) ? align256(mfa::gemm_partial_bytes(p)) : 0;
+}
+
+size_t mfa_oproj_workspace_size(int B, mfa_dtype dt) {
+  if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(dt)) return 0;
+  return oproj_ws(B, dt, nullptr);
+}
+
+int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_bytes, int B, mfa_dtype dt,
+              void* stream) {
+  if (!attn || !w_o || !y || B < 1 || B > MFA_MAX_BATCH) return MFA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(dt)) return MFA_ERR_UNSUPPORTED;
+  if (!aligned16(attn) || !aligned16(w_o) || !aligned16(y) || !aligned16(ws)) return MFA_ERR_ALIGNMENT;
+  mfa::GemmPlan plan;
+  const size_t need = oproj_ws(B, dt, &plan);
+  if (need > 0 && (!ws || ws_bytes < need)) return MFA_ERR_WORKSPACE;
+  const bool bf = dt == MFA_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  if (bf && plan.splits > 1) {
+    hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s));
+  }
+  return hip_status(mfa::launch_gemm(bf, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s));
+}
+
+}  // extern "C"

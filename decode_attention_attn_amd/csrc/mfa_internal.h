@@ -1,0 +1,82 @@
+// Host-side interface between the C ABI (mfa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace mfa {
+
+// Launch and return this launch's own status (not a stale error of earlier
+// work). Arguments are converted to the kernel's parameter types first.
+template <typename... Params, size_t... I>
+inline hipError_t launch_impl(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                              std::tuple<Params...>& vals, std::index_sequence<I...>) {
+  void* ptrs[] = {(void*)&std::get<I>(vals)...};
+  return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+}
+template <typename... Params, typename... Args>
+inline hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel arity");
+  std::tuple<Params...> vals(static_cast<Params>(args)...);
+  return launch_impl(kernel, grid, block, stream, vals, std::index_sequence_for<Params...>{});
+}
+
+// ------------------------------------------------------------------ attention
+enum class AttnKind { F32, BF16, BF16_FP8KV };
+
+struct AttnLaunch {
+  AttnKind kind;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int64_t* seq_off;
+  const int32_t* seq_len;
+  void* out;
+  float* lse;
+  void* ws;
+  int B;
+  int G;  // workgroups of the main kernel
+  float softmax_scale, k_scale, v_scale;
+};
+
+// Partials: [G + B][64][256] fp32 outputs then [G + B][64] fp32 lse.
+inline size_t attn_part_o_bytes(int B, int G) { return (size_t)(G + B) * 64 * 256 * sizeof(float); }
+inline size_t attn_ws_bytes(int B, int G) {
+  return attn_part_o_bytes(B, G) + (size_t)(G + B) * 64 * sizeof(float);
+}
+
+hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream);
+
+// ------------------------------------------------------------------ projections
+// Y[M, N] = X[M, K] * W^T where W = [W0 (N0 rows); W1 (N - N0 rows)], each [rows, K].
+enum class GemmOut {
+  Partial,  // fp32 partial sums [S][M][N] (S = split count) into the workspace
+  Direct    // final values [M][N] in the activation dtype
+};
+
+struct GemmPlan {
+  int M, N, K, N0;
+  int splits;   // S
+  int mchunks;  // ceil(M / 128) (bf16 path)
+};
+
+// bf16: MFMA kernel; f32: VALU kernel (no split).
+GemmPlan plan_gemm(bool bf16, int M, int N, int K, int N0);
+size_t gemm_partial_bytes(const GemmPlan& p);
+hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
+                       GemmOut mode, hipStream_t stream);
+
+// c_hat[M, N] = rmsnorm(sum_s part[s]) * gamma, in the activation dtype.
+hipError_t launch_rmsnorm_reduce(bool bf16, const float* part, int S, int M, int N, const float* gamma,
+                                 float eps, void* out, hipStream_t stream);
+// out[M, N] = sum_s part[s], in the activation dtype.
+hipError_t launch_sum_reduce(bool bf16, const float* part, int S, int M, int N, void* out, hipStream_t stream);
+// rows m: k = sum_s part[s][m][0:256], v = sum_s part[s][m][256:512] written at cache row off[m] + len[m].
+hipError_t launch_kv_scatter(bool bf16, const float* part, int S, int M, void* k_cache, void* v_cache,
+                             const int64_t* seq_off, const int32_t* seq_len, hipStream_t stream);
+
+}  // namespace mfa

@@ -1,0 +1,302 @@
+// Projection kernels of the MFA decode layer on gfx950: the low-rank query
+// path (7168 -> 2048 -> RMSNorm -> 16384), the shared K/V projections
+// (7168 -> 256 each, appended to the cache) and the out-projection
+// (16384 -> 7168). Step-3 paper summary, "Method": the decode cost model
+// counts these as the "linear projections" term.
+//
+// At decode time M = batch is small (2..128) and every weight byte is used M
+// times, so these products are bound by streaming the weights from HBM. The
+// bf16 kernel therefore tiles 128 weight rows x 128 batch rows per workgroup,
+// stages both operands through a 4-deep LDS ring filled by direct-to-LDS DMA
+// (weights read exactly once, as 128 B runs), and multiplies with
+// v_mfma_f32_16x16x32_bf16. The weight tile is the MFMA A operand, so each
+// lane ends up with four consecutive output columns of one batch row (one
+// 16-byte store). When the output tile count alone cannot fill the GPU, the
+// K dimension is split and fp32 partial sums go to the workspace; a small
+// epilogue kernel adds them and applies what follows the product (RMSNorm of
+// the latent, the cache-row scatter of K/V, or the cast of y).
+// The fp32 path (used for exact-ish parity at tiny batch) is a VALU GEMV.
+#include "mfa_common.h"
+#include "mfa_internal.h"
+
+namespace mfa {
+
+constexpr int kGN = 128;    // output columns (weight rows) per workgroup
+constexpr int kGM = 128;    // batch rows per workgroup
+constexpr int kGK = 64;     // K per stage
+constexpr int kGStages = 4;
+constexpr int kGTileBytes = 128 * kGK * 2;        // 16 KB: one operand tile
+constexpr int kGStageBytes = 2 * kGTileBytes;     // weights then activations
+constexpr int kGDmaPerWave = 2 * (kGTileBytes / 1024) / 4;  // 8
+constexpr int kGSteadyVm = (kGStages - 2) * kGDmaPerWave;   // 16
+
+struct GemmArgs {
+  const bf16* X;
+  const bf16* W0;
+  const bf16* W1;
+  void* Y;
+  int M, N, K, N0, S;
+};
+
+// 16-byte chunk swizzle for 128-byte rows: conflict-free ds_read_b128 of 16
+// consecutive rows at one logical chunk for 32- and 64-bank LDS.
+__device__ __forceinline__ int gswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, int kc, char* stage, int w, int lane) {
+  const int r_in = lane >> 3;  // 8 rows of 128 B per 1 KB block
+  const int pc = lane & 7;
+  const int k0 = kc * kGK;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int blk = 4 * w + jj;
+    const int r = 8 * blk + r_in;
+    const int c = pc ^ gswz(r);
+    const int n = n0 + r;
+    const bf16* wrow = n < a.N0 ? a.W0 + (long long)n * a.K : a.W1 + (long long)(n - a.N0) * a.K;
+    __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
+    int m = m0 + r;
+    m = m < a.M ? m : a.M - 1;
+    const bf16* xrow = a.X + (long long)m * a.K;
+    __builtin_amdgcn_global_load_lds((const void*)(xrow + k0 + c * 8),
+                                     (MFA_LDS void*)(stage + kGTileBytes + blk * 1024), 16, 0, 0);
+  }
+}
+
+template <GemmOut MODE>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ring[kGStages * kGStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = blockIdx.x * kGN;
+  const int split = blockIdx.y;
+  const int m0 = blockIdx.z * kGM;
+  const int nch = a.K / kGK;
+  const int c_begin = (int)((long long)split * nch / a.S);
+  const int c_end = (int)((long long)(split + 1) * nch / a.S);
+  const int nloc = c_end - c_begin;
+
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < kGStages - 1; ++s)
+    if (issued < nloc) {
+      gemm_issue(a, n0, m0, c_begin + issued, ring + s * kGStageBytes, w, lane);
+      ++issued;
+    }
+
+  for (int t = 0; t < nloc; ++t) {
+    if (issued - t - 1 >= kGStages - 2)
+      wait_vmcnt<kGSteadyVm>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (issued < nloc) {
+      gemm_issue(a, n0, m0, c_begin + issued, ring + ((t + kGStages - 1) % kGStages) * kGStageBytes, w, lane);
+      ++issued;
+    }
+    const char* ws = ring + (t % kGStages) * kGStageBytes;
+    const char* xs = ws + kGTileBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 4 * j + g;
+      bf16x8 wa[8], xb[2];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int r = 16 * nb + i16;
+        wa[nb] = *(const MFA_LDS bf16x8*)(ws + r * 128 + ((c ^ gswz(r)) << 4));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = 16 * (2 * w + mi) + i16;
+        xb[mi] = *(const MFA_LDS bf16x8*)(xs + r * 128 + ((c ^ gswz(r)) << 4));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+          acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nb], xb[mi], acc[mi][nb], 0, 0, 0);
+    }
+  }
+
+  // lane (i16, g), register i of acc[mi][nb] = Y[m0 + 16(2w+mi) + i16][n0 + 16nb + 4g + i]
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int m = m0 + 16 * (2 * w + mi) + i16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const int n = n0 + 16 * nb + 4 * g;
+      if constexpr (MODE == GemmOut::Partial) {
+        float* dst = (float*)a.Y + ((long long)split * a.M + m) * a.N + n;
+        *(f32x4*)dst = acc[mi][nb];
+      } else {
+        bf16* dst = (bf16*)a.Y + (long long)m * a.N + n;
+        const bf16x4 o = {(bf16)acc[mi][nb][0], (bf16)acc[mi][nb][1], (bf16)acc[mi][nb][2], (bf16)acc[mi][nb][3]};
+        *(bf16x4*)dst = o;
+      }
+    }
+  }
+}
+
+// fp32 GEMV-style product: one wave per output column, rows of X in groups of 4.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const float* W0, const float* W1, float* Y,
+                                                       int M, int N, int K, int N0) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const float* wrow = n < N0 ? W0 + (long long)n * K : W1 + (long long)(n - N0) * K;
+  for (int mb = 0; mb < M; mb += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 4 * lane; k < K; k += 256) {
+      const f32x4 wv = *(const f32x4*)(wrow + k);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        if (mb + mi < M) {
+          const f32x4 xv = *(const f32x4*)(X + (long long)(mb + mi) * K + k);
+          acc[mi] = fmaf(wv[0], xv[0], acc[mi]);
+          acc[mi] = fmaf(wv[1], xv[1], acc[mi]);
+          acc[mi] = fmaf(wv[2], xv[2], acc[mi]);
+          acc[mi] = fmaf(wv[3], xv[3], acc[mi]);
+        }
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      float v = acc[mi];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0 && mb + mi < M) Y[(long long)(mb + mi) * N + n] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ epilogues
+template <typename OutT>
+__global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* part, int S, int M, int N,
+                                                             const float* gamma, float eps, OutT* out) {
+  // one block per row; N <= 4096 and N % 256 == 0
+  const int m = blockIdx.x;
+  const int t = threadIdx.x;
+  float c[16];
+  float ss = 0.f;
+  const int per = N / 256;
+  for (int i = 0; i < per; ++i) {
+    const int col = t + 256 * i;
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[((long long)s * M + m) * N + col];
+    c[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  __shared__ float red[4];
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float r = rsqrtf(tot / (float)N + eps);
+  for (int i = 0; i < per; ++i) {
+    const int col = t + 256 * i;
+    float v = c[i] * r;
+    if (gamma != nullptr) v *= gamma[col];
+    out[(long long)m * N + col] = (OutT)v;
+  }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void sum_reduce_kernel(const float* part, int S, int M, int N, OutT* out) {
+  const long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
+  const long long total4 = (long long)M * N / 4;
+  if (i4 >= total4) return;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) v += *(const f32x4*)(part + (long long)s * M * N + 4 * i4);
+  OutT* dst = out + 4 * i4;
+  dst[0] = (OutT)v[0];
+  dst[1] = (OutT)v[1];
+  dst[2] = (OutT)v[2];
+  dst[3] = (OutT)v[3];
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(128) void kv_scatter_kernel(const float* part, int S, int M, OutT* kc, OutT* vc,
+                                                         const int64_t* seq_off, const int32_t* seq_len) {
+  const int m = blockIdx.x;
+  const int col = 4 * threadIdx.x;  // 0..508 of the [k | v] row
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) v += *(const f32x4*)(part + ((long long)s * M + m) * 512 + col);
+  const long long row = seq_off[m] + (long long)seq_len[m];
+  OutT* dst = (col < 256 ? kc : vc) + row * 256 + (col & 255);
+  dst[0] = (OutT)v[0];
+  dst[1] = (OutT)v[1];
+  dst[2] = (OutT)v[2];
+  dst[3] = (OutT)v[3];
+}
+
+// ------------------------------------------------------------------ host side
+GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0) {
+  GemmPlan p{M, N, K, N0, 1, 1};
+  if (!bf16_path) return p;
+  p.mchunks = (M + kGM - 1) / kGM;
+  const int tiles = (N / kGN) * p.mchunks;
+  const int nch = K / kGK;
+  // split K only until about half the CUs have a workgroup: partial sums cost
+  // 2 * S * M * N * 4 bytes of extra traffic.
+  int s = (128 + tiles - 1) / tiles;
+  if (s < 1) s = 1;
+  if (s > nch) s = nch;
+  p.splits = s;
+  return p;
+}
+
+size_t gemm_partial_bytes(const GemmPlan& p) { return (size_t)p.splits * p.M * p.N * sizeof(float); }
+
+hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
+                       GemmOut mode, hipStream_t stream) {
+  if (!bf16_path) {
+    return launch(gemm_f32_kernel, dim3((p.N + 3) / 4), dim3(256), stream, (const float*)X, (const float*)W0,
+                       (const float*)W1, (float*)Y, p.M, p.N, p.K, p.N0);
+  }
+  GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits};
+  const dim3 grid(p.N / kGN, p.splits, p.mchunks);
+  if (mode == GemmOut::Partial)
+    return launch(gemm_bf16_kernel<GemmOut::Partial>, grid, dim3(256), stream, a);
+  else
+    return launch(gemm_bf16_kernel<GemmOut::Direct>, grid, dim3(256), stream, a);
+}
+
+hipError_t launch_rmsnorm_reduce(bool bf16_path, const float* part, int S, int M, int N, const float* gamma, float eps,
+                                 void* out, hipStream_t stream) {
+  if (bf16_path)
+    return launch(rmsnorm_reduce_kernel<bf16>, dim3(M), dim3(256), stream, part, S, M, N, gamma, eps,
+                       (bf16*)out);
+  else
+    return launch(rmsnorm_reduce_kernel<float>, dim3(M), dim3(256), stream, part, S, M, N, gamma, eps,
+                       (float*)out);
+}
+
+hipError_t launch_sum_reduce(bool bf16_path, const float* part, int S, int M, int N, void* out, hipStream_t stream) {
+  const long long total4 = (long long)M * N / 4;
+  const dim3 grid((unsigned)((total4 + 255) / 256));
+  if (bf16_path)
+    return launch(sum_reduce_kernel<bf16>, grid, dim3(256), stream, part, S, M, N, (bf16*)out);
+  else
+    return launch(sum_reduce_kernel<float>, grid, dim3(256), stream, part, S, M, N, (float*)out);
+}
+
+hipError_t launch_kv_scatter(bool bf16_path, const float* part, int S, int M, void* k_cache, void* v_cache,
+                             const int64_t* seq_off, const int32_t* seq_len, hipStream_t stream) {
+  if (bf16_path)
+    return launch(kv_scatter_kernel<bf16>, dim3(M), dim3(128), stream, part, S, M, (bf16*)k_cache,
+                       (bf16*)v_cache, seq_off, seq_len);
+  else
+    return launch(kv_scatter_kernel<float>, dim3(M), dim3(128), stream, part, S, M, (float*)k_cache,
+                       (float*)v_cache, seq_off, seq_len);
+}
+
+}  // namespace mfa

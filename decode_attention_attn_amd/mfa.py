@@ -1,0 +1,147 @@
+"""Python binding of libmfa (ctypes): the C entry points under the same names.
+
+Argument marshalling only: torch tensors are passed as device pointers
+(``data_ptr()``), sizes and scalars as host values, the stream as the current
+torch stream unless given. Every step of the computation runs in the HIP
+kernels of ``libmfa.so``; there is no fallback. Importing this module raises
+``ImportError`` when the library has not been built
+(``python -m decode_attention_attn_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmfa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libmfa.so not built at {LIB_PATH}; run `python -m decode_attention_attn_amd.build`")
+try:
+    _lib = ctypes.CDLL(LIB_PATH)
+except OSError as e:  # pragma: no cover - depends on the ROCm install
+    raise ImportError(f"cannot load {LIB_PATH}: {e}") from e
+
+# mfa_dtype
+MFA_F32, MFA_BF16, MFA_FP8_E4M3 = 0, 1, 2
+# status codes
+MFA_OK, MFA_ERR_INVALID_ARG, MFA_ERR_UNSUPPORTED, MFA_ERR_ALIGNMENT, MFA_ERR_WORKSPACE, MFA_ERR_HIP = 0, -1, -2, -3, -4, -5
+MFA_HIDDEN, MFA_RANK, MFA_HEADS, MFA_HEAD_DIM = 7168, 2048, 64, 256
+MFA_QDIM = MFA_HEADS * MFA_HEAD_DIM
+MFA_MAX_BATCH = 65536
+
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_lib.mfa_version.restype = _I
+_lib.mfa_version.argtypes = []
+_lib.mfa_status_string.restype = ctypes.c_char_p
+_lib.mfa_status_string.argtypes = [_I]
+_lib.mfa_qproj_workspace_size.restype = _Z
+_lib.mfa_qproj_workspace_size.argtypes = [_I, _I]
+_lib.mfa_qproj.restype = _I
+_lib.mfa_qproj.argtypes = [_P, _P, _P, _F, _P, _P, _P, _Z, _I, _I, _P]
+_lib.mfa_kv_append_workspace_size.restype = _Z
+_lib.mfa_kv_append_workspace_size.argtypes = [_I, _I]
+_lib.mfa_kv_append.restype = _I
+_lib.mfa_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]
+_lib.mfa_decode_attn_workspace_size.restype = _Z
+_lib.mfa_decode_attn_workspace_size.argtypes = [_I, _I]
+_lib.mfa_decode_attn.restype = _I
+_lib.mfa_decode_attn.argtypes = [_P, _P, _P, _P, _P, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
+_lib.mfa_oproj_workspace_size.restype = _Z
+_lib.mfa_oproj_workspace_size.argtypes = [_I, _I]
+_lib.mfa_oproj.restype = _I
+_lib.mfa_oproj.argtypes = [_P, _P, _P, _P, _Z, _I, _I, _P]
+
+EXPORTED = [
+    "mfa_version", "mfa_status_string",
+    "mfa_qproj_workspace_size", "mfa_qproj",
+    "mfa_kv_append_workspace_size", "mfa_kv_append",
+    "mfa_decode_attn_workspace_size", "mfa_decode_attn",
+    "mfa_oproj_workspace_size", "mfa_oproj",
+]
+
+
+class MfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {mfa_status_string(status)} ({status})")
+        self.status = status
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    if t is None:
+        return 0
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def check(status: int, where: str = "libmfa") -> None:
+    if status != MFA_OK:
+        raise MfaError(status, where)
+
+
+def mfa_version() -> int:
+    return _lib.mfa_version()
+
+
+def mfa_status_string(status: int) -> str:
+    return _lib.mfa_status_string(status).decode()
+
+
+def mfa_qproj_workspace_size(B: int, dt: int) -> int:
+    return _lib.mfa_qproj_workspace_size(B, dt)
+
+
+def mfa_qproj(x, w_dq, gamma, eps, w_uq, q_out, ws, B, dt, stream=None) -> int:
+    return _lib.mfa_qproj(_ptr(x), _ptr(w_dq), _ptr(gamma), eps, _ptr(w_uq), _ptr(q_out), _ptr(ws), _nbytes(ws),
+                          B, dt, _stream(stream))
+
+
+def mfa_kv_append_workspace_size(B: int, act_dt: int) -> int:
+    return _lib.mfa_kv_append_workspace_size(B, act_dt)
+
+
+def mfa_kv_append(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, ws, B, act_dt, cache_dt, stream=None) -> int:
+    return _lib.mfa_kv_append(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off),
+                              _ptr(seq_len), _ptr(ws), _nbytes(ws), B, act_dt, cache_dt, _stream(stream))
+
+
+def mfa_decode_attn_workspace_size(B: int, num_workgroups: int = 0) -> int:
+    return _lib.mfa_decode_attn_workspace_size(B, num_workgroups)
+
+
+def mfa_decode_attn(q, k_cache, v_cache, seq_off, seq_len, softmax_scale, k_scale, v_scale, out, lse, ws, B,
+                    num_workgroups, q_dt, kv_dt, stream=None) -> int:
+    return _lib.mfa_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off), _ptr(seq_len),
+                                softmax_scale, k_scale, v_scale, _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), B,
+                                num_workgroups, q_dt, kv_dt, _stream(stream))
+
+
+def mfa_oproj_workspace_size(B: int, dt: int) -> int:
+    return _lib.mfa_oproj_workspace_size(B, dt)
+
+
+def mfa_oproj(attn, w_o, y, ws, B, dt, stream=None) -> int:
+    return _lib.mfa_oproj(_ptr(attn), _ptr(w_o), _ptr(y), _ptr(ws), _nbytes(ws), B, dt, _stream(stream))
+
+
+def raw_function(name: str):
+    """The ctypes function object of an exported symbol (for ABI tests)."""
+    return getattr(_lib, name)

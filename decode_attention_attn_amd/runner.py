@@ -1,0 +1,147 @@
+"""Device plumbing around the libmfa binding: upload stored inputs, allocate
+outputs and workspaces with torch, call the C entry points on one stream.
+
+No arithmetic of the method happens here; torch only provides device memory
+and the stream.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import mfa
+from .inputs import BF16, F32, FP8
+
+SOFTMAX_SCALE = 1.0 / math.sqrt(256.0)
+
+_DT = {F32: mfa.MFA_F32, BF16: mfa.MFA_BF16, FP8: mfa.MFA_FP8_E4M3}
+
+
+def to_device(arr: np.ndarray, kind: str, device="cuda") -> torch.Tensor:
+    """Stored numpy array -> torch tensor holding the same bytes on ``device``."""
+    arr = np.ascontiguousarray(arr)
+    if kind == F32:
+        t = torch.from_numpy(arr.astype(np.float32, copy=False))
+    elif kind == BF16:
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    elif kind == FP8:
+        t = torch.from_numpy(arr.astype(np.uint8, copy=False))
+    elif kind == "i64":
+        t = torch.from_numpy(arr.astype(np.int64, copy=False))
+    elif kind == "i32":
+        t = torch.from_numpy(arr.astype(np.int32, copy=False))
+    else:
+        raise ValueError(kind)
+    return t.to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Device tensor (fp32 or bf16) -> exact float64 numpy copy."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def dtype_code(kind: str) -> int:
+    return _DT[kind]
+
+
+def _act_torch(kind):
+    return torch.float32 if kind == F32 else torch.bfloat16
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def upload_attn(inp: dict, device="cuda") -> dict:
+    return dict(
+        q=to_device(inp["q"], inp["kind_q"], device),
+        k=to_device(inp["k_cache"], inp["kind_kv"], device),
+        v=to_device(inp["v_cache"], inp["kind_kv"], device),
+        off=to_device(inp["seq_off"], "i64", device),
+        len=to_device(inp["seq_len"], "i32", device),
+        kind_q=inp["kind_q"], kind_kv=inp["kind_kv"],
+        k_scale=float(inp["k_scale"]) if inp["k_scale"] is not None else 1.0,
+        v_scale=float(inp["v_scale"]) if inp["v_scale"] is not None else 1.0,
+        B=len(inp["seq_len"]),
+    )
+
+
+class AttnCall:
+    """Preallocated outputs + workspace for repeated mfa_decode_attn calls."""
+
+    def __init__(self, dev: dict, num_workgroups: int = 0, want_lse: bool = True, stream=None):
+        self.dev = dev
+        self.G = num_workgroups
+        B = dev["B"]
+        device = dev["q"].device
+        self.out = torch.empty((B, 64, 256), dtype=_act_torch(dev["kind_q"]), device=device)
+        self.lse = torch.empty((B, 64), dtype=torch.float32, device=device) if want_lse else None
+        self.ws = _ws(mfa.mfa_decode_attn_workspace_size(B, num_workgroups), device)
+        self.stream = stream
+
+    def __call__(self, k=None, v=None):
+        d = self.dev
+        st = mfa.mfa_decode_attn(d["q"], d["k"] if k is None else k, d["v"] if v is None else v, d["off"], d["len"],
+                                 SOFTMAX_SCALE, d["k_scale"], d["v_scale"], self.out, self.lse, self.ws, d["B"],
+                                 self.G, _DT[d["kind_q"]], _DT[d["kind_kv"]], self.stream)
+        mfa.check(st, "mfa_decode_attn")
+        return self.out, self.lse
+
+
+def decode_attn(inp: dict, num_workgroups: int = 0, device="cuda"):
+    """Upload, run once, synchronize; returns (out, lse, device inputs)."""
+    dev = upload_attn(inp, device)
+    call = AttnCall(dev, num_workgroups)
+    out, lse = call()
+    torch.cuda.synchronize()
+    return out, lse, dev
+
+
+def upload_layer(inp: dict, device="cuda") -> dict:
+    ka, kk = inp["kind_act"], inp["kind_kv"]
+    d = {n: to_device(inp[n], ka, device) for n in ("x", "w_dq", "w_uq", "w_k", "w_v", "w_o")}
+    d.update(k=to_device(inp["k_cache"], kk, device), v=to_device(inp["v_cache"], kk, device),
+             off=to_device(inp["seq_off"], "i64", device), len=to_device(inp["seq_len"], "i32", device),
+             kind_act=ka, kind_kv=kk, B=len(inp["seq_len"]), eps=float(inp.get("eps", 1e-6)))
+    return d
+
+
+class LayerCall:
+    """One decode step of the attention layer: q path, K/V append, attention, out-projection."""
+
+    def __init__(self, dev: dict, num_workgroups: int = 0, stream=None):
+        self.dev = dev
+        B = dev["B"]
+        device = dev["x"].device
+        at = _act_torch(dev["kind_act"])
+        dt = _DT[dev["kind_act"]]
+        self.dt = dt
+        self.G = num_workgroups
+        self.stream = stream
+        self.q = torch.empty((B, 64, 256), dtype=at, device=device)
+        self.o = torch.empty((B, 64, 256), dtype=at, device=device)
+        self.lse = torch.empty((B, 64), dtype=torch.float32, device=device)
+        self.y = torch.empty((B, 7168), dtype=at, device=device)
+        self.len_after = torch.empty_like(dev["len"])
+        self.ws_q = _ws(mfa.mfa_qproj_workspace_size(B, dt), device)
+        self.ws_kv = _ws(mfa.mfa_kv_append_workspace_size(B, dt), device)
+        self.ws_a = _ws(mfa.mfa_decode_attn_workspace_size(B, num_workgroups), device)
+        self.ws_o = _ws(mfa.mfa_oproj_workspace_size(B, dt), device)
+
+    def __call__(self):
+        d, dt, s = self.dev, self.dt, self.stream
+        B = d["B"]
+        mfa.check(mfa.mfa_qproj(d["x"], d["w_dq"], None, d["eps"], d["w_uq"], self.q, self.ws_q, B, dt, s),
+                  "mfa_qproj")
+        mfa.check(mfa.mfa_kv_append(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"], self.ws_kv, B,
+                                    dt, _DT[d["kind_kv"]], s), "mfa_kv_append")
+        # the appended row is attended: length + 1 (the caller owns seq_len)
+        torch.add(d["len"], 1, out=self.len_after)
+        mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE, 1.0, 1.0,
+                                      self.o, self.lse, self.ws_a, B, self.G, dt, _DT[d["kind_kv"]], s),
+                  "mfa_decode_attn")
+        mfa.check(mfa.mfa_oproj(self.o, d["w_o"], self.y, self.ws_o, B, dt, s), "mfa_oproj")
+        return self

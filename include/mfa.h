@@ -1,0 +1,139 @@
+/*
+ * libmfa — decode-time Multi-Matrix Factorization Attention (MFA) on AMD
+ * Instinct MI355X (gfx950). C ABI.
+ *
+ * What is computed (Step-3 paper, "Step-3 is Large yet Affordable: Model-system
+ * Co-design for Cost-effective Decoding"; summary page on bud-325.pages.dev,
+ * sections "Key claims" and "Method"; redeep.blog Step3 post, architecture
+ * table): per new token the hidden state (7168) is down-projected to a 2048-wide
+ * latent, normalized, and up-projected to 64 query heads of width 256; all 64
+ * heads attend over ONE shared K head and ONE shared V head of width 256 held
+ * in a per-sequence cache (one K row and one V row per token); the 64 head
+ * outputs are projected back to 7168.
+ *
+ * Choices where the pages are silent: the normalization is RMSNorm
+ * (x * rsqrt(mean(x^2) + eps) * gamma); the softmax scale is a parameter
+ * (1/sqrt(256) = 0.0625 for this model); no rotary/positional term; no biases;
+ * weights are row-major [out, in] (y = x W^T); query column n is head n / 256,
+ * channel n % 256, and the attention output is flattened the same way.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers the caller allocated; the library
+ *    never allocates, frees or keeps them. Scalars and sizes are host values.
+ *  - Tensors are dense row-major. Each pointer must be 16-byte aligned.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous: no call synchronizes. Results are valid once the stream
+ *    reaches them.
+ *  - Calls return MFA_OK or a negative status and never abort. Argument
+ *    checks (null pointers, sizes, dtype combinations, alignment, workspace
+ *    size) run on the host before any HIP call. A failed launch returns
+ *    MFA_ERR_HIP. Device-side preconditions (documented per call) are not
+ *    checked.
+ *  - Calls on different streams or threads are independent; the library keeps
+ *    no state besides a cached per-device property table.
+ */
+#ifndef MFA_H_
+#define MFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Model dimensions (fixed by the architecture). */
+#define MFA_HIDDEN 7168
+#define MFA_RANK 2048
+#define MFA_HEADS 64
+#define MFA_HEAD_DIM 256
+#define MFA_QDIM (MFA_HEADS * MFA_HEAD_DIM) /* 16384 */
+
+/* Storage types. MFA_BF16 is bfloat16; MFA_FP8_E4M3 is the OCP 8-bit E4M3
+ * ("fn": max 448, no infinity) with one fp32 scale per tensor (value = byte
+ * value * scale). */
+typedef enum { MFA_F32 = 0, MFA_BF16 = 1, MFA_FP8_E4M3 = 2 } mfa_dtype;
+
+enum {
+  MFA_OK = 0,
+  MFA_ERR_INVALID_ARG = -1, /* null pointer, size out of range */
+  MFA_ERR_UNSUPPORTED = -2, /* dtype combination not provided */
+  MFA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
+  MFA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  MFA_ERR_HIP = -5          /* a HIP runtime call or launch failed */
+};
+
+/* Largest batch any call accepts. */
+#define MFA_MAX_BATCH 65536
+
+int mfa_version(void);                       /* 10000 * major + 100 * minor + patch */
+const char* mfa_status_string(int status);   /* static string, never NULL */
+
+/* ------------------------------------------------------------------ q path
+ * Low-rank query (Step-3 summary, "Method": 7168 -> 2048, normalized, -> 64 x 256).
+ *   c     = x W_dq^T                      x [B, 7168], W_dq [2048, 7168]
+ *   c_hat = c * rsqrt(mean(c^2) + eps) * gamma   (gamma [2048] fp32, NULL = ones)
+ *   q     = c_hat W_uq^T as [B, 64, 256]  W_uq [16384, 2048]
+ * dt = MFA_F32 (all fp32) or MFA_BF16 (x, weights, q in bf16; fp32
+ * accumulation; c_hat is rounded to bf16 before the up-projection).
+ * ws: device scratch of at least mfa_qproj_workspace_size(B, dt) bytes
+ * (contents undefined on return). 1 <= B <= MFA_MAX_BATCH.
+ */
+size_t mfa_qproj_workspace_size(int B, mfa_dtype dt);
+int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq,
+              void* q_out, void* ws, size_t ws_bytes, int B, mfa_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------ K/V append
+ * The new token's shared K and V rows (Step-3 summary, "Method": one K and one
+ * V per token): k = x W_k^T, v = x W_v^T (W_k, W_v [256, 7168]), written to
+ * rows seq_off[b] + seq_len[b] of k_cache / v_cache ([rows, 256], cache_dt).
+ * seq_off (int64) and seq_len (int32) are device arrays of length B; seq_len
+ * is NOT modified (the caller advances it before attending). Supported:
+ * act_dt = cache_dt = MFA_F32, or act_dt = cache_dt = MFA_BF16.
+ * Device-side precondition: the target rows exist and are distinct.
+ * ws: at least mfa_kv_append_workspace_size(B, act_dt) bytes.
+ */
+size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt);
+int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
+                  const int64_t* seq_off, const int32_t* seq_len, void* ws, size_t ws_bytes, int B,
+                  mfa_dtype act_dt, mfa_dtype cache_dt, void* stream);
+
+/* ------------------------------------------------------------------ attention
+ * Shared-KV decode attention (Step-3 summary, "Key claims"/"Method": 64 query
+ * heads attend over one shared K and one shared V head of width 256). For each
+ * sequence b and head h, over cache rows j in [seq_off[b], seq_off[b]+seq_len[b]):
+ *   s_j = (q[b,h,:] . K_j) * softmax_scale * k_scale
+ *   out[b,h,:] = sum_j softmax(s)_j * V_j * v_scale
+ *   lse[b,h]   = ln sum_j exp(s_j)           (natural log; optional output)
+ * A sequence with seq_len 0 yields out = 0 and lse = -inf.
+ * Supported (q_dt, kv_dt): (F32, F32) -> fp32 out; (BF16, BF16) -> bf16 out;
+ * (BF16, FP8_E4M3) -> bf16 out. k_scale / v_scale are used for FP8_E4M3 only
+ * (pass 1 otherwise). q [B, 64, 256]; caches [rows, 256]; out [B, 64, 256];
+ * lse [B, 64] fp32 or NULL. seq_off/seq_len as for mfa_kv_append.
+ * The key range of all sequences is cut into equal contiguous pieces, one per
+ * workgroup; sequences cut into several pieces are merged by log-sum-exp.
+ * num_workgroups: 0 = one per compute unit (the default), > 0 forces that many
+ * (tests use 1 to disable all splitting). ws: at least
+ * mfa_decode_attn_workspace_size(B, num_workgroups) bytes; with
+ * num_workgroups = 0 this queries the current device.
+ */
+size_t mfa_decode_attn_workspace_size(int B, int num_workgroups);
+int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                    const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale,
+                    void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups,
+                    mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
+
+/* ------------------------------------------------------------------ out-projection
+ * y = O_flat W_o^T: attn [B, 16384] (the [B, 64, 256] attention output),
+ * W_o [7168, 16384], y [B, 7168]. dt = MFA_F32 or MFA_BF16 (fp32 accumulation).
+ * ws: at least mfa_oproj_workspace_size(B, dt) bytes.
+ */
+size_t mfa_oproj_workspace_size(int B, mfa_dtype dt);
+int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_bytes, int B,
+              mfa_dtype dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFA_H_ */

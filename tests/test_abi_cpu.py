@@ -1,0 +1,99 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/mfa.h, and rejects invalid calls on the host before any
+HIP call (only failing validations are exercised here, so no kernel can
+launch)."""
+
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+mfa = pytest.importorskip("decode_attention_attn_amd.mfa", reason="libmfa.so not built")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+MIS = 0x10001   # misaligned
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mfa.h")).read()
+    return sorted(set(re.findall(r"\b(mfa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported():
+    declared = _declared()
+    assert set(declared) == set(mfa.EXPORTED)
+    for name in declared:
+        assert mfa.raw_function(name) is not None
+
+
+def test_version_and_status_strings():
+    assert mfa.mfa_version() == 10000
+    for code in (0, -1, -2, -3, -4, -5):
+        assert mfa.mfa_status_string(code).startswith("MFA_")
+    assert "unknown" in mfa.mfa_status_string(7)
+
+
+def test_workspace_sizes():
+    B, G = 32, 256
+    assert mfa.mfa_decode_attn_workspace_size(B, G) == (G + B) * 64 * 256 * 4 + (G + B) * 64 * 4
+    assert mfa.mfa_decode_attn_workspace_size(0, G) == 0
+    assert mfa.mfa_decode_attn_workspace_size(B, -1) == 0
+    for fn in (mfa.mfa_qproj_workspace_size, mfa.mfa_kv_append_workspace_size):
+        for dt in (mfa.MFA_F32, mfa.MFA_BF16):
+            assert fn(2, dt) > 0 and fn(128, dt) >= fn(2, dt)
+        assert fn(2, mfa.MFA_FP8_E4M3) == 0
+        assert fn(0, mfa.MFA_BF16) == 0
+    assert mfa.mfa_oproj_workspace_size(2, mfa.MFA_F32) == 0
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, off=FAKE, len=FAKE, scale=0.0625, ks=1.0, vs=1.0, out=FAKE, lse=None,
+             ws=FAKE, ws_bytes=1 << 40, B=4, G=8, qdt=mfa.MFA_BF16, kvdt=mfa.MFA_BF16)
+    a.update(kw)
+    f = mfa.raw_function("mfa_decode_attn")
+    return f(a["q"], a["k"], a["v"], a["off"], a["len"], a["scale"], a["ks"], a["vs"], a["out"], a["lse"], a["ws"],
+             a["ws_bytes"], a["B"], a["G"], a["qdt"], a["kvdt"], None)
+
+
+def test_decode_attn_rejects_bad_arguments():
+    assert _attn(q=None) == mfa.MFA_ERR_INVALID_ARG
+    assert _attn(len=None) == mfa.MFA_ERR_INVALID_ARG
+    assert _attn(B=0) == mfa.MFA_ERR_INVALID_ARG
+    assert _attn(B=mfa.MFA_MAX_BATCH + 1) == mfa.MFA_ERR_INVALID_ARG
+    assert _attn(G=-1) == mfa.MFA_ERR_INVALID_ARG
+    assert _attn(scale=float("nan")) == mfa.MFA_ERR_INVALID_ARG
+    assert _attn(qdt=mfa.MFA_F32, kvdt=mfa.MFA_BF16) == mfa.MFA_ERR_UNSUPPORTED
+    assert _attn(qdt=mfa.MFA_FP8_E4M3, kvdt=mfa.MFA_FP8_E4M3) == mfa.MFA_ERR_UNSUPPORTED
+    assert _attn(qdt=7) == mfa.MFA_ERR_UNSUPPORTED
+    assert _attn(k=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert _attn(out=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert _attn(off=FAKE + 4) == mfa.MFA_ERR_ALIGNMENT
+    assert _attn(ws=None) == mfa.MFA_ERR_WORKSPACE
+    need = mfa.mfa_decode_attn_workspace_size(4, 8)
+    assert _attn(ws_bytes=need - 1) == mfa.MFA_ERR_WORKSPACE
+
+
+def test_projections_reject_bad_arguments():
+    qp = mfa.raw_function("mfa_qproj")
+    assert qp(None, FAKE, None, 1e-6, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_F32, None) == mfa.MFA_ERR_INVALID_ARG
+    assert qp(FAKE, FAKE, None, -1.0, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_F32, None) == mfa.MFA_ERR_INVALID_ARG
+    assert qp(FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_FP8_E4M3, None) == mfa.MFA_ERR_UNSUPPORTED
+    assert qp(FAKE, MIS, None, 1e-6, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_BF16, None) == mfa.MFA_ERR_ALIGNMENT
+    need = mfa.mfa_qproj_workspace_size(2, mfa.MFA_BF16)
+    assert qp(FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, need - 1, 2, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
+    kv = mfa.raw_function("mfa_kv_append")
+    args = [FAKE] * 8
+    assert kv(*args, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_FP8_E4M3, None) == mfa.MFA_ERR_UNSUPPORTED
+    assert kv(*args, 1 << 30, 2, mfa.MFA_F32, mfa.MFA_BF16, None) == mfa.MFA_ERR_UNSUPPORTED
+    assert kv(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_BF16,
+              None) == mfa.MFA_ERR_INVALID_ARG
+    assert kv(*args, 0, 2, mfa.MFA_BF16, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
+    op = mfa.raw_function("mfa_oproj")
+    assert op(FAKE, FAKE, None, FAKE, 1 << 30, 2, mfa.MFA_BF16, None) == mfa.MFA_ERR_INVALID_ARG
+    assert op(FAKE, FAKE, FAKE, FAKE, 1 << 30, 0, mfa.MFA_BF16, None) == mfa.MFA_ERR_INVALID_ARG
+    assert op(FAKE, MIS, FAKE, FAKE, 1 << 30, 2, mfa.MFA_BF16, None) == mfa.MFA_ERR_ALIGNMENT
+    need = mfa.mfa_oproj_workspace_size(128, mfa.MFA_BF16)
+    if need > 0:
+        assert op(FAKE, FAKE, FAKE, FAKE, need - 1, 128, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
