@@ -19,11 +19,23 @@ std::atomic<int> g_cu_count[kMaxDevices];
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned_n(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
 
+thread_local int g_last_hip_error = 0;
+
+// HIP failures map to MFA_ERR_HIP; the HIP code is kept for mfa_last_hip_error()
+// and printed when MFA_DEBUG is set.
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MFA_OK;
+  g_last_hip_error = (int)e;
+  if (getenv("MFA_DEBUG")) fprintf(stderr, "libmfa: HIP error %d: %s\n", (int)e, hipGetErrorString(e));
+  return MFA_ERR_HIP;
+}
+
 // Compute units of the current device (cached per device).
 int current_cu_count(int* status) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
-    *status = MFA_ERR_HIP;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    *status = hip_status(e != hipSuccess ? e : hipErrorInvalidDevice);
     return 0;
   }
   if (dev < kMaxDevices) {
@@ -31,8 +43,9 @@ int current_cu_count(int* status) {
     if (c > 0) return c;
   }
   int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
-    *status = MFA_ERR_HIP;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0) {
+    *status = hip_status(e != hipSuccess ? e : hipErrorInvalidDevice);
     return 0;
   }
   if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
@@ -43,18 +56,14 @@ bool act_dtype_ok(mfa_dtype dt) { return dt == MFA_F32 || dt == MFA_BF16; }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// HIP failures map to MFA_ERR_HIP; with MFA_DEBUG set the HIP error is printed.
-int hip_status(hipError_t e) {
-  if (e == hipSuccess) return MFA_OK;
-  if (getenv("MFA_DEBUG")) fprintf(stderr, "libmfa: HIP error %d: %s\n", (int)e, hipGetErrorString(e));
-  return MFA_ERR_HIP;
-}
 
 }  // namespace
 
 extern "C" {
 
 int mfa_version(void) { return 10000 * 1 + 100 * 0 + 0; }
+
+int mfa_last_hip_error(void) { return g_last_hip_error; }
 
 const char* mfa_status_string(int status) {
   switch (status) {
@@ -103,10 +112,7 @@ int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, co
   e = mfa::launch_rmsnorm_reduce(bf, part, bf ? plan.splits : 1, B, MFA_RANK, gamma, eps, chat, s);
   if (e != hipSuccess) return hip_status(e);
   const mfa::GemmPlan up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM);
-  if (bf && up.splits != 1) {
-    // the up-projection has 128 column tiles per 128 rows: never split
-    return MFA_ERR_HIP;
-  }
+  if (bf && up.splits != 1) return hip_status(hipErrorInvalidConfiguration);  // never: 128 column tiles
   e = mfa::launch_gemm(bf, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s);
   return hip_status(e);
 }

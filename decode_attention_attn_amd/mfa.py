@@ -15,6 +15,15 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmfa.so")
 
+# PyTorch-ROCm ships its own HIP runtime (libamdhip64.so, soname .so.7). Load it
+# before libmfa.so so that libmfa's dependency resolves to that same runtime;
+# loading libmfa first would bring in a second HIP runtime from /opt/rocm whose
+# streams and allocations are foreign to torch's.
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - torch is a dependency of the binding
+    pass
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libmfa.so not built at {LIB_PATH}; run `python -m decode_attention_attn_amd.build`")
 try:
@@ -36,6 +45,8 @@ _lib.mfa_version.restype = _I
 _lib.mfa_version.argtypes = []
 _lib.mfa_status_string.restype = ctypes.c_char_p
 _lib.mfa_status_string.argtypes = [_I]
+_lib.mfa_last_hip_error.restype = _I
+_lib.mfa_last_hip_error.argtypes = []
 _lib.mfa_qproj_workspace_size.restype = _Z
 _lib.mfa_qproj_workspace_size.argtypes = [_I, _I]
 _lib.mfa_qproj.restype = _I
@@ -54,7 +65,7 @@ _lib.mfa_oproj.restype = _I
 _lib.mfa_oproj.argtypes = [_P, _P, _P, _P, _Z, _I, _I, _P]
 
 EXPORTED = [
-    "mfa_version", "mfa_status_string",
+    "mfa_version", "mfa_status_string", "mfa_last_hip_error",
     "mfa_qproj_workspace_size", "mfa_qproj",
     "mfa_kv_append_workspace_size", "mfa_kv_append",
     "mfa_decode_attn_workspace_size", "mfa_decode_attn",
@@ -64,7 +75,8 @@ EXPORTED = [
 
 class MfaError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {mfa_status_string(status)} ({status})")
+        detail = f" [hipError_t {mfa_last_hip_error()}]" if status == MFA_ERR_HIP else ""
+        super().__init__(f"{where}: {mfa_status_string(status)} ({status}){detail}")
         self.status = status
 
 
@@ -103,6 +115,10 @@ def mfa_version() -> int:
 
 def mfa_status_string(status: int) -> str:
     return _lib.mfa_status_string(status).decode()
+
+
+def mfa_last_hip_error() -> int:
+    return _lib.mfa_last_hip_error()
 
 
 def mfa_qproj_workspace_size(B: int, dt: int) -> int:

@@ -68,6 +68,7 @@ enum {
 
 int mfa_version(void);                       /* 10000 * major + 100 * minor + patch */
 const char* mfa_status_string(int status);   /* static string, never NULL */
+int mfa_last_hip_error(void);                /* hipError_t behind this thread's last MFA_ERR_HIP (0 if none) */
 
 /* ------------------------------------------------------------------ q path
  * Low-rank query (Step-3 summary, "Method": 7168 -> 2048, normalized, -> 64 x 256).

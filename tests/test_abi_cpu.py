@@ -97,3 +97,10 @@ def test_projections_reject_bad_arguments():
     need = mfa.mfa_oproj_workspace_size(128, mfa.MFA_BF16)
     if need > 0:
         assert op(FAKE, FAKE, FAKE, FAKE, need - 1, 128, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
+
+
+def test_single_hip_runtime_in_process():
+    # libmfa must bind to the HIP runtime torch already loaded, not a second copy
+    maps = open(f"/proc/{os.getpid()}/maps").read()
+    runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes
