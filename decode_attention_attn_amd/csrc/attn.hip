@@ -10,17 +10,17 @@
 //
 // Design (MI355X-first):
 //  * Work split. The key ranges of all sequences are laid end to end and cut
-//    into G equal pieces (G = one workgroup per CU), each a multiple of the
-//    32-row tile. A workgroup walks its piece, which may cover the tail of one
-//    sequence and the head of the next. Ragged lengths therefore never leave
-//    CUs idle. A sequence cut into several pieces is merged afterwards by a
+//    into G equal pieces (G = one workgroup per CU), each a multiple of 64
+//    rows. A workgroup walks its piece, which may cover the tail of one
+//    sequence and the head of the next, so ragged lengths never leave CUs
+//    idle. A sequence cut into several pieces is merged afterwards by a
 //    log-sum-exp combine; a sequence inside one piece is written directly.
-//  * Data path. K/V tiles (32 rows) go HBM -> LDS by direct-to-LDS DMA
-//    (global_load_lds_dwordx4: each lane moves 16 B, a wave moves 1 KB = 2
-//    bf16 rows) into a 4-stage (bf16) or 8-stage (fp8) ring, three or seven
-//    tiles ahead of the compute, one barrier per tile. Rows are XOR-swizzled
-//    in 16-byte chunks at DMA time so that the MFMA operand reads below are
-//    bank-conflict free; every row is still read as whole 512 B (256 B) runs.
+//  * Data path. Tiles of 32 KB (32 bf16 rows or 64 fp8 rows of K, then of V)
+//    go HBM -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4: each lane
+//    moves 16 B, a wave 1 KB) into a 4-stage ring, three tiles ahead of the
+//    compute, one barrier per tile. Rows are XOR-swizzled in 16-byte chunks at
+//    DMA time so that the MFMA operand reads below are bank-conflict free;
+//    every row is still read as one full run.
 //  * Math. The 64 heads are the dense M dimension. Wave w owns heads
 //    16w..16w+15. Scores are computed transposed, S^T = K Q^T with
 //    v_mfma_f32_16x16x32_bf16 (K from LDS with ds_read_b128, Q^T resident in
@@ -32,10 +32,11 @@
 //    pass exists. fp8 cache bytes are widened to bf16 in registers
 //    (v_cvt_scalef32_pk_bf16_fp8, exact); the per-tensor scales are folded
 //    into the score multiplier (K) and the final normalisation (V).
-//  * Softmax in base 2: scores are multiplied by scale*log2(e) once, the
-//    running max/sum live in registers, the O accumulator is rescaled when the
-//    max moves, and the row sums are reduced across the 4 lanes of a head only
-//    at the end of a piece.
+//  * Softmax in base 2: scores are multiplied by scale*log2(e) once; the
+//    running max and sum live in registers; the reference max moves only when
+//    a score exceeds it by more than 8 (a factor 256), so the O accumulator is
+//    rescaled on a piece's first tile and rarely after; row sums are combined
+//    across the 4 lanes of a head with the gfx950 row swaps at piece end.
 #include "mfa_common.h"
 #include "mfa_internal.h"
 
@@ -49,7 +50,7 @@ struct AttnArgs {
   const int32_t* seq_len;
   void* out;
   float* lse;
-  float* part_o;    // [G + B][64][256] fp32, normalized partial outputs
+  void* part_o;     // [G + B][64][256] normalized partial outputs (bf16 for the MFMA kernels, fp32 otherwise)
   float* part_lse;  // [G + B][64] fp32, base-2 log-sum-exp of each partial
   int B;
   int G;
@@ -57,63 +58,76 @@ struct AttnArgs {
   float v_mul;      // v_scale
 };
 
-constexpr int kTile = 32;  // cache rows per tile (all kernels use the same piece granularity)
+constexpr int kPieceAlign = 64;  // piece lengths are multiples of this many rows
 
 // ---------------------------------------------------------------------------
 // Work split shared by the attention kernels and the combine kernel. Every
 // wave computes it redundantly from seq_len (B small), so no inter-wave sync.
-__device__ __forceinline__ long long total_len(const int32_t* len, int B, int lane) {
-  long long s = 0;
-  for (int i = lane; i < B; i += 64) s += len[i];
-  return wave_sum_ll(s);
-}
-
 __device__ __forceinline__ long long piece_len(long long total, int G) {
   long long per = (total + G - 1) / G;
-  return (per + kTile - 1) / kTile * kTile;
+  return (per + kPieceAlign - 1) / kPieceAlign * kPieceAlign;
 }
 
-// First sequence whose key range contains global position r0 and that
-// sequence's start. Requires 0 <= r0 < total.
-__device__ __forceinline__ void find_seq(const int32_t* len, int B, long long r0, int lane, int& b_out,
-                                         long long& start_out) {
-  long long base = 0;
+// Workgroup w takes piece w. (Placing the pieces of a sequence on one XCD, to
+// share its L2, measured no faster: the cache stream dominates and spreading
+// each sequence over all XCDs balances their memory paths.)
+__device__ __forceinline__ int piece_index(int /*G*/) { return blockIdx.x; }
+
+// Total length, plus the sequence containing global position r0 and its start
+// (only when 0 <= r0 < total). One pass over seq_len for B <= 256.
+__device__ __forceinline__ void scan_lengths(const int32_t* len, int B, int G, int wgi, int lane,
+                                             long long& total, long long& per, long long& r0, int& b_out,
+                                             long long& start_out) {
+  constexpr int kCached = 4;
+  long long vals[kCached];
+  long long s = 0;
+#pragma unroll
+  for (int c = 0; c < kCached; ++c) {
+    const int i = 64 * c + lane;
+    vals[c] = i < B ? (long long)len[i] : 0;
+    s += vals[c];
+  }
+  for (int i = 64 * kCached + lane; i < B; i += 64) s += len[i];
+  total = uniform(wave_sum_ll(s));
+  per = piece_len(total, G);
+  r0 = (long long)wgi * per;
   b_out = B - 1;
   start_out = 0;
-  for (int c0 = 0; c0 < B; c0 += 64) {
+  if (r0 >= total) return;
+  long long base = 0;
+  for (int c0 = 0, c = 0; c0 < B; c0 += 64, ++c) {
     const int idx = c0 + lane;
-    const long long v = idx < B ? (long long)len[idx] : 0;
+    long long v;
+    if (c < kCached) {
+      v = vals[0];
+#pragma unroll
+      for (int k = 1; k < kCached; ++k) v = (c == k) ? vals[k] : v;
+    } else {
+      v = idx < B ? (long long)len[idx] : 0;
+    }
     long long incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      long long t = __shfl_up(incl, o);
+      const long long t = __shfl_up(incl, o);
       if (lane >= o) incl += t;
     }
     const unsigned long long hit = __ballot(idx < B && base + incl > r0);
     if (hit) {
       const int first = __ffsll((long long)hit) - 1;
-      const long long incl_f = __shfl(incl, first);
-      const long long v_f = __shfl(v, first);
-      b_out = c0 + first;
-      start_out = base + incl_f - v_f;
+      b_out = uniform(c0 + first);
+      start_out = uniform(base + __shfl(incl, first) - __shfl(v, first));
       return;
     }
     base += __shfl(incl, 63);
   }
 }
 
-// Exclusive prefix of len[0..b).
-__device__ __forceinline__ long long seq_start_of(const int32_t* len, int b, int lane) {
-  long long s = 0;
-  for (int i = lane; i < b; i += 64) s += len[i];
-  return wave_sum_ll(s);
-}
-
 // Walks one workgroup's piece tile by tile (wave-uniform state).
+template <int kRows>
 struct Cursor {
-  long long gpos, r1;              // next global position, end of the workgroup's piece
-  long long seq_start, seq_end;    // global range of the current sequence
-  long long off;                   // cache row of the sequence's first key
+  long long gpos, r1;            // next global position, end of the workgroup's piece
+  long long seq_start, seq_end;  // global range of the current sequence
+  long long off;                 // cache row of the sequence's first key
   int b;
 
   __device__ __forceinline__ bool valid() const { return gpos < r1; }
@@ -121,13 +135,13 @@ struct Cursor {
   // Rows [lo, hi) of the current tile, relative to the sequence start.
   __device__ __forceinline__ void tile(long long& lo, long long& hi) const {
     lo = gpos - seq_start;
-    long long e = gpos + kTile;
+    const long long e = gpos + kRows;
     const long long pe = part_end();
     hi = (e < pe ? e : pe) - seq_start;
   }
   __device__ __forceinline__ void advance(const int32_t* len, const int64_t* offs) {
     const long long pe = part_end();
-    long long e = gpos + kTile;
+    const long long e = gpos + kRows;
     gpos = e < pe ? e : pe;
     if (gpos == seq_end && gpos < r1) {
       do {
@@ -140,20 +154,18 @@ struct Cursor {
   }
 };
 
-__device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wg, int lane, Cursor& c) {
-  const long long total = uniform(total_len(a.seq_len, a.B, lane));
-  const long long per = piece_len(total, a.G);
-  const long long r0 = (long long)wg * per;
+template <int kRows>
+__device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane, Cursor<kRows>& c) {
+  long long total, per, r0, start;
+  int b;
+  scan_lengths(a.seq_len, a.B, a.G, wgi, lane, total, per, r0, b, start);
   if (r0 >= total) return false;
   c.r1 = r0 + per < total ? r0 + per : total;
   c.gpos = r0;
-  int b;
-  long long start;
-  find_seq(a.seq_len, a.B, r0, lane, b, start);
-  c.b = uniform(b);
-  c.seq_start = uniform(start);
-  c.seq_end = c.seq_start + load_scalar(a.seq_len, c.b);
-  c.off = load_scalar(a.seq_off, c.b);
+  c.b = b;
+  c.seq_start = start;
+  c.seq_end = start + load_scalar(a.seq_len, b);
+  c.off = load_scalar(a.seq_off, b);
   return true;
 }
 
@@ -162,42 +174,50 @@ __device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wg, int lane,
 template <bool FP8>
 struct Cfg {
   static constexpr int kRowBytes = FP8 ? 256 : 512;
-  static constexpr int kTileBytes = kTile * kRowBytes;            // one of K or V
-  static constexpr int kStageBytes = 2 * kTileBytes;              // K then V
-  static constexpr int kStages = FP8 ? 8 : 4;
-  static constexpr int kBlocks = kTileBytes / 1024;               // 1 KB DMA blocks per K (or V) tile
-  static constexpr int kRowsPerBlock = 1024 / kRowBytes;          // 2 (bf16) / 4 (fp8)
-  static constexpr int kDmaPerWave = 2 * kBlocks / 4;             // DMA instructions per wave per tile
-  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;   // DMAs allowed in flight after a tile landed
+  static constexpr int kRows = FP8 ? 64 : 32;                     // cache rows per tile
+  static constexpr int kHalfBytes = kRows * kRowBytes;             // K (or V) part of a tile: 16 KB
+  static constexpr int kTileBytes = 2 * kHalfBytes;                // 32 KB
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kRowsPerBlock = 1024 / kRowBytes;           // rows per 1 KB DMA block
+  static constexpr int kBlocksPerWave = kHalfBytes / 1024 / 4;     // DMA blocks per wave per half: 4
+  static constexpr int kDmaPerWave = 2 * kBlocksPerWave;           // DMA instructions per wave per tile: 8
+  static constexpr int kStages = 4;                                // LDS ring: 3 tiles in flight
+  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;    // DMAs still in flight once a tile landed
 };
 
-// XOR swizzles of 16-byte chunks within a tile row (row r = 0..31 of the tile).
+// XOR swizzles of 16-byte chunks within a row (row r = 0..31 of a 32-row block).
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v16(int r) { return (r & 7) << 1; }
 __device__ __forceinline__ int swz_v8(int r) { return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3); }
 
+// Direct-to-LDS DMA of the producer's current tile into a ring stage. Lane i of
+// a wave moves 16 bytes into LDS slot i of a 1 KB block, so the XOR swizzle is
+// applied on the global side: slot (row r, chunk pc) receives global chunk
+// pc ^ swz(r). Each row is still read as one full run. Rows past the valid
+// end re-read the last valid row (their scores are masked to -inf).
 template <bool FP8>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor& c, char* stage, int w, int lane) {
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<FP8>::kRows>& c, char* stage, int w,
+                                           int lane) {
   using C = Cfg<FP8>;
   long long lo, hi;
   c.tile(lo, hi);
   const char* kb = (const char*)a.k + (c.off + lo) * C::kRowBytes;
   const char* vb = (const char*)a.v + (c.off + lo) * C::kRowBytes;
   const int nvalid = (int)(hi - lo);
-  constexpr int kChunks = C::kRowBytes / 16;
-  const int r_in = FP8 ? (lane >> 4) : (lane >> 5);
-  const int pc = lane & (kChunks - 1);
+  const int r_in = lane / C::kChunksPerRow;
+  const int pc = lane % C::kChunksPerRow;
 #pragma unroll
-  for (int jj = 0; jj < C::kBlocks / 4; ++jj) {
-    const int blk = w * (C::kBlocks / 4) + jj;
+  for (int jj = 0; jj < C::kBlocksPerWave; ++jj) {
+    const int blk = w * C::kBlocksPerWave + jj;
     const int r = blk * C::kRowsPerBlock + r_in;
-    const int rr = r < nvalid ? r : nvalid - 1;  // clamp: masked rows re-read a valid row
-    const int ck = pc ^ swz_k(r);
-    const int cv = pc ^ (FP8 ? swz_v8(r) : swz_v16(r));
+    const int rr = r < nvalid ? r : nvalid - 1;
+    const int r32 = r & 31;
+    const int ck = pc ^ swz_k(r32);
+    const int cv = pc ^ (FP8 ? swz_v8(r32) : swz_v16(r32));
     __builtin_amdgcn_global_load_lds((const void*)(kb + (long long)rr * C::kRowBytes + ck * 16),
                                      (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(vb + (long long)rr * C::kRowBytes + cv * 16),
-                                     (MFA_LDS void*)(stage + C::kTileBytes + blk * 1024), 16, 0, 0);
+                                     (MFA_LDS void*)(stage + C::kHalfBytes + blk * 1024), 16, 0, 0);
   }
 }
 
@@ -212,108 +232,166 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int w, int n, i
   }
 }
 
-// K operand (A of S^T = K Q^T) for the 32 rows of a tile: kf[pb][j] holds the
-// 8 channels of k-slot group g at step j for row 16pb + n.
+// K operand (A of S^T = K Q^T) for rows 16pb..16pb+15 of the 32-row block at
+// ks: kf[j] holds the 8 channels of k-slot group g at step j for row 16pb + n.
 template <bool FP8>
-__device__ __forceinline__ void read_k(const char* ks, int n, int g, bf16x8 (&kf)[2][8]) {
+__device__ __forceinline__ void read_k(const char* ks, int n, int g, bf16x8 (&kf)[8], int pb) {
   if constexpr (!FP8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int pc = ((4 * j + g) ^ n) << 4;
-      kf[0][j] = *(const MFA_LDS bf16x8*)(ks + n * 512 + pc);
-      kf[1][j] = *(const MFA_LDS bf16x8*)(ks + (16 + n) * 512 + pc);
-    }
+    for (int j = 0; j < 8; ++j) kf[j] = *(const MFA_LDS bf16x8*)(ks + (16 * pb + n) * 512 + (((4 * j + g) ^ n) << 4));
   } else {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int pc = ((4 * jj + g) ^ n) << 4;
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-        const u32x4 r = *(const MFA_LDS u32x4*)(ks + (16 * pb + n) * 256 + pc);
-        fp8x4_to_bf16(r[0], kf[pb][2 * jj], 0);
-        fp8x4_to_bf16(r[1], kf[pb][2 * jj], 4);
-        fp8x4_to_bf16(r[2], kf[pb][2 * jj + 1], 0);
-        fp8x4_to_bf16(r[3], kf[pb][2 * jj + 1], 4);
-      }
+      const u32x4 r = *(const MFA_LDS u32x4*)(ks + (16 * pb + n) * 256 + (((4 * jj + g) ^ n) << 4));
+      fp8x4_to_bf16(r[0], kf[2 * jj], 0);
+      fp8x4_to_bf16(r[1], kf[2 * jj], 4);
+      fp8x4_to_bf16(r[2], kf[2 * jj + 1], 0);
+      fp8x4_to_bf16(r[3], kf[2 * jj + 1], 4);
     }
   }
 }
 
-// V^T operand (A of O^T = V^T P^T): vf[db] holds, for channel 16db + n, the
-// cache rows of k-slots 8g..8g+7, i.e. rows 16b + 4g + i (b = 0,1; i = 0..3).
+// V^T operand (A of O^T = V^T P^T): the fragment of channel block db holds,
+// for channel 16db + n, the cache rows of k-slots 8g..8g+7, i.e. rows
+// 16b + 4g + i (b = 0,1; i = 0..3) of the 32-row block.
 template <bool FP8>
-__device__ __forceinline__ void read_v(const char* vs, int n, int g, bf16x8 (&vf)[16]) {
-  if constexpr (!FP8) {
-    // tr16: lane i of a 16-lane group supplies row 4g + i/4 (+16), channels 4(i%4)..+3
-    const int rq = n >> 2;
-    const int half = (n & 1) << 3;
-    const int lc_lo = (n & 3) >> 1;
-    const int r0 = 4 * g + rq, r1 = 16 + 4 * g + rq;
-    const int base0 = r0 * 512 + half, base1 = r1 * 512 + half;
-    const int sw0 = swz_v16(r0), sw1 = swz_v16(r1);
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
+struct VReader {
+  int base0, base1, sw0, sw1, lc_lo;  // bf16 (tr16: two reads of 4 rows)
+  int base, sw;                       // fp8 (tr8: one read of 8 rows)
+  __device__ __forceinline__ VReader(int n, int g) {
+    if constexpr (!FP8) {
+      // lane i of a 16-lane group supplies row 4g + i/4 (+16), channels 4(i%4)..+3
+      const int rq = n >> 2;
+      const int half = (n & 1) << 3;
+      lc_lo = (n & 3) >> 1;
+      const int r0 = 4 * g + rq, r1 = 16 + 4 * g + rq;
+      base0 = r0 * 512 + half;
+      base1 = r1 * 512 + half;
+      sw0 = swz_v16(r0);
+      sw1 = swz_v16(r1);
+    } else {
+      // lane i of a 16-lane group supplies k-slot row r' = i/2, byte half i&1
+      const int rp = n >> 1;
+      const int r = 16 * (rp >> 2) + 4 * g + (rp & 3);
+      base = r * 256 + ((n & 1) << 3);
+      sw = swz_v8(r);
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const char* vs, int db) const {
+    if constexpr (!FP8) {
       const int lc = 2 * db + lc_lo;
       const bf16x4 lo = lds_read_tr16((const MFA_LDS bf16x4*)(vs + base0 + ((lc ^ sw0) << 4)));
       const bf16x4 hi = lds_read_tr16((const MFA_LDS bf16x4*)(vs + base1 + ((lc ^ sw1) << 4)));
-      vf[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-  } else {
-    // tr8: lane i of a 16-lane group supplies k-slot row r' = i/2, byte half i&1
-    const int rp = n >> 1;
-    const int r = 16 * (rp >> 2) + 4 * g + (rp & 3);
-    const int base = r * 256 + ((n & 1) << 3);
-    const int sw = swz_v8(r);
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
       const i32x2 raw = lds_read_tr8((const MFA_LDS i32x2*)(vs + base + ((db ^ sw) << 4)));
-      fp8x4_to_bf16((unsigned)raw[0], vf[db], 0);
-      fp8x4_to_bf16((unsigned)raw[1], vf[db], 4);
+      bf16x8 v;
+      fp8x4_to_bf16((unsigned)raw[0], v, 0);
+      fp8x4_to_bf16((unsigned)raw[1], v, 4);
+      return v;
     }
   }
+};
+
+// One 32-row block: scores, online softmax update, PV accumulate.
+template <bool FP8>
+__device__ __forceinline__ void attend_block(const char* ks, const char* vs, int nvalid, int n, int g,
+                                             const VReader<FP8>& vr, const bf16x8 (&qf)[8], float score_mul,
+                                             float& m_run, float& l_run, f32x4 (&acc)[16]) {
+  // K fragments first, then the score MFMAs interleaved with the V reads (V
+  // does not depend on the scores), so that LDS latency overlaps matrix work.
+  bf16x8 kf0[8], kf1[8];
+  read_k<FP8>(ks, n, g, kf0, 0);
+  read_k<FP8>(ks, n, g, kf1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 vf[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[j], qf[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[j], qf[j], s1, 0, 0, 0);
+    vf[2 * j] = vr.read(vs, 2 * j);
+    vf[2 * j + 1] = vr.read(vs, 2 * j + 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = (4 * g + i < nvalid) ? s0[i] * score_mul : -INFINITY;
+    sc[4 + i] = (16 + 4 * g + i < nvalid) ? s1[i] * score_mul : -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mx = max_over_rows(mx);
+  // Lazy rescale: the reference max only moves when a score exceeds it by
+  // more than 8 (base 2), so exponentials stay <= 256 (no bf16/fp32 range
+  // issue) and the O rescale runs on a piece's first block and rarely after.
+  const bool jump = mx > m_run + 8.f;
+  if (__ballot(jump)) {
+    const float m_new = jump ? mx : m_run;
+    const float alpha = fast_exp2(m_run - m_new);  // 0 on a fresh piece (m_run = -inf)
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) acc[db] *= alpha;
+    m_run = m_new;
+  }
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fast_exp2(sc[i] - m_run);
+    l_run += p[i];
+  }
+  const bf16x8 pf = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3], (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, acc[db], 0, 0, 0);
 }
 
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   using C = Cfg<FP8>;
-  __shared__ __attribute__((aligned(1024))) char ring[C::kStages * C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char ring[C::kStages * C::kTileBytes];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int wg = blockIdx.x;
+  const int wgi = piece_index(a.G);
 
-  Cursor prod;
-  if (!init_cursor(a, wg, lane, prod)) return;
-  Cursor cons = prod;
+  Cursor<C::kRows> prod;
+  if (!init_cursor(a, wgi, lane, prod)) return;
+  Cursor<C::kRows> cons = prod;
 
+  // Q of the first piece goes out together with the first tile DMAs.
+  bf16x8 qf[8];
+  load_q<FP8>(a, cons.b, w, n, g, qf);
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s) {
     if (prod.valid()) {
-      issue_tile<FP8>(a, prod, ring + s * C::kStageBytes, w, lane);
+      issue_tile<FP8>(a, prod, ring + s * C::kTileBytes, w, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
   }
+  // A full wait here (Q and the prologue tiles arrive together): a partial
+  // wait would leave Q looking pending to the compiler, which would then
+  // drain the ring before every score product in the loop.
+  wait_vmcnt<0>();
 
-  bf16x8 qf[8];
   f32x4 acc[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const VReader<FP8> vr(n, g);
   float m_run = -INFINITY, l_run = 0.f;
-  long long piece_lo = 0;
-  bool fresh = true;
-  bool drained = false;  // stores issued since the last wait: next wait drains fully
+  long long piece_lo = cons.gpos - cons.seq_start;
+  bool fresh = false;
+  bool drained = false;  // stores were issued since the last wait: drain fully
 
   for (int t = 0; cons.valid(); ++t) {
     if (fresh) {
-      // Wait for this Q right away (a full drain at each piece start): a
-      // pending Q load would otherwise make every later wait drain the ring.
+      // Later pieces of the workgroup: a full drain for their Q (rare).
       load_q<FP8>(a, cons.b, w, n, g, qf);
       wait_vmcnt<0>();
-#pragma unroll
-      for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run = -INFINITY;
-      l_run = 0.f;
+      m_run = -INFINITY;  // the first block rescales acc by exp2(-inf) = 0
       piece_lo = cons.gpos - cons.seq_start;
       fresh = false;
     }
@@ -324,64 +402,25 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     drained = false;
     __builtin_amdgcn_s_barrier();
     if (prod.valid()) {
-      issue_tile<FP8>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kStageBytes, w, lane);
+      issue_tile<FP8>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, w, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
-
+    char* stage = ring + (t % C::kStages) * C::kTileBytes;
     long long lo, hi;
     cons.tile(lo, hi);
     const int nvalid = (int)(hi - lo);
-    const char* ks = ring + (t % C::kStages) * C::kStageBytes;
-
-    bf16x8 kf[2][8];
-    read_k<FP8>(ks, n, g, kf);
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][j], qf[j], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][j], qf[j], s1, 0, 0, 0);
+    attend_block<FP8>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
+    if constexpr (FP8) {
+      if (nvalid > 32)
+        attend_block<FP8>(stage + 32 * C::kRowBytes, stage + C::kHalfBytes + 32 * C::kRowBytes, nvalid - 32, n, g,
+                          vr, qf, a.score_mul, m_run, l_run, acc);
     }
-    // V reads do not depend on the scores: issue them before the softmax.
-    bf16x8 vf[16];
-    read_v<FP8>(ks + C::kTileBytes, n, g, vf);
-
-    float sc[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = (4 * g + i < nvalid) ? s0[i] * a.score_mul : -INFINITY;
-      sc[4 + i] = (16 + 4 * g + i < nvalid) ? s1[i] * a.score_mul : -INFINITY;
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(sc[i] - m_new);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {  // the running max moved for some head of this wave
-#pragma unroll
-      for (int db = 0; db < 16; ++db) acc[db] *= alpha;
-    }
-    const bf16x8 pf = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3],
-                       (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
-#pragma unroll
-    for (int db = 0; db < 16; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, acc[db], 0, 0, 0);
 
     const long long pe = cons.part_end() - cons.seq_start;
     if (hi == pe) {
       // finalize this piece of sequence cons.b
-      float lt = l_run + __shfl_xor(l_run, 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = sum_over_rows(l_run);
       const float inv = a.v_mul / lt;
       const float lse2 = m_run + fast_log2(lt);
       const int h = 16 * w + n;
@@ -396,10 +435,16 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
         }
         if (a.lse != nullptr && g == 0) a.lse[(long long)cons.b * kHeads + h] = lse2 * kLn2;
       } else {
-        const long long slot = (long long)wg + cons.b;
-        float* prow = a.part_o + (slot * kHeads + h) * kHeadDim + 4 * g;
+        // partial outputs in bf16: half the bytes of the round trip through
+        // memory; the merge weights (lse) stay fp32
+        const long long slot = (long long)wgi + cons.b;
+        bf16* prow = (bf16*)a.part_o + (slot * kHeads + h) * kHeadDim + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) *(f32x4*)(prow + 16 * db) = acc[db] * inv;
+        for (int db = 0; db < 16; ++db) {
+          const bf16x4 o = {(bf16)(acc[db][0] * inv), (bf16)(acc[db][1] * inv), (bf16)(acc[db][2] * inv),
+                            (bf16)(acc[db][3] * inv)};
+          *(bf16x4*)(prow + 16 * db) = o;
+        }
         if (g == 0) a.part_lse[slot * kHeads + h] = lse2;
       }
       fresh = true;
@@ -412,14 +457,16 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 kernel (fp32 q and cache): plain VALU dot products, same work split and
 // partial format. Lane (n, g) of wave w owns head 16w+n and channels 64g..64g+63.
+constexpr int kF32Rows = 32;
+
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int wg = blockIdx.x;
-  Cursor cons;
-  if (!init_cursor(a, wg, lane, cons)) return;
+  const int wgi = piece_index(a.G);
+  Cursor<kF32Rows> cons;
+  if (!init_cursor(a, wgi, lane, cons)) return;
   const int h = 16 * w + n;
 
   float qr[64], acc[64];
@@ -432,7 +479,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < 64; d += 4) {
         const f32x4 v = *(const f32x4*)(qrow + d);
-        qr[d] = v[0]; qr[d + 1] = v[1]; qr[d + 2] = v[2]; qr[d + 3] = v[3];
+        qr[d] = v[0];
+        qr[d + 1] = v[1];
+        qr[d + 2] = v[2];
+        qr[d + 3] = v[3];
       }
 #pragma unroll
       for (int d = 0; d < 64; ++d) acc[d] = 0.f;
@@ -446,9 +496,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int nvalid = (int)(hi - lo);
     const float* kb = (const float*)a.k + (cons.off + lo) * kHeadDim + 64 * g;
     const float* vb = (const float*)a.v + (cons.off + lo) * kHeadDim + 64 * g;
-    float s[kTile];
+    float s[kF32Rows];
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < kF32Rows; ++j) {
       s[j] = -INFINITY;
       if (j < nvalid) {
         float part = 0.f;
@@ -467,14 +517,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     }
     float mx = s[0];
 #pragma unroll
-    for (int j = 1; j < kTile; ++j) mx = fmaxf(mx, s[j]);
+    for (int j = 1; j < kF32Rows; ++j) mx = fmaxf(mx, s[j]);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = fast_exp2(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int d = 0; d < 64; ++d) acc[d] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < kF32Rows; ++j) {
       if (j < nvalid) {
         const float pj = fast_exp2(s[j] - m_new);
         l_run += pj;
@@ -501,8 +551,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         dst = (float*)a.out + ((long long)cons.b * kHeads + h) * kHeadDim + 64 * g;
         if (a.lse != nullptr && g == 0) a.lse[(long long)cons.b * kHeads + h] = lse2 * kLn2;
       } else {
-        const long long slot = (long long)wg + cons.b;
-        dst = a.part_o + (slot * kHeads + h) * kHeadDim + 64 * g;
+        const long long slot = (long long)wgi + cons.b;
+        dst = (float*)a.part_o + (slot * kHeads + h) * kHeadDim + 64 * g;
         if (g == 0) a.part_lse[slot * kHeads + h] = lse2;
       }
 #pragma unroll
@@ -515,53 +565,77 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the pieces of each split sequence. Grid (B, 4): block
-// (b, hg) merges heads 16hg..16hg+15; thread t owns head 16hg + t/16 and
-// channels 16*(t%16)..+15. Sequences inside one piece were written by the
-// attention kernel and are skipped; empty sequences get out = 0, lse = -inf.
-template <typename OutT>
+// Log-sum-exp merge of the pieces of each split sequence. Grid (B, 16): block
+// (b, hq) merges heads 4hq..4hq+3; thread t owns head 4hq + t/64 and channels
+// 4*(t%64)..+3. Sequences inside one piece were written by the attention
+// kernel and are skipped; empty sequences get out = 0, lse = -inf. Partials
+// are read 8 at a time and merged with a running max (one pass).
+__device__ __forceinline__ f32x4 load4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+template <typename OutT, typename PartT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int h = 16 * blockIdx.y + (threadIdx.x >> 4);
-  const int d0 = 16 * (threadIdx.x & 15);
-  const long long L = a.seq_len[b];
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  const int d0 = 4 * lane;
+  const long long L = load_scalar(a.seq_len, b);
   OutT* orow = (OutT*)a.out + ((long long)b * kHeads + h) * kHeadDim + d0;
   if (L == 0) {
 #pragma unroll
-    for (int d = 0; d < 16; ++d) orow[d] = (OutT)0.f;
-    if (a.lse != nullptr && (threadIdx.x & 15) == 0) a.lse[(long long)b * kHeads + h] = -INFINITY;
+    for (int d = 0; d < 4; ++d) orow[d] = (OutT)0.f;
+    if (a.lse != nullptr && lane == 0) a.lse[(long long)b * kHeads + h] = -INFINITY;
     return;
   }
-  const long long total = total_len(a.seq_len, a.B, lane);
+  // total length and this sequence's start in one pass over seq_len
+  long long s_all = 0, s_before = 0;
+  for (int i = lane; i < a.B; i += 64) {
+    const long long v = a.seq_len[i];
+    s_all += v;
+    s_before += i < b ? v : 0;
+  }
+  const long long total = uniform(wave_sum_ll(s_all));
+  const long long start = uniform(wave_sum_ll(s_before));
   const long long per = piece_len(total, a.G);
-  const long long start = seq_start_of(a.seq_len, b, lane);
   const long long w0 = start / per, w1 = (start + L - 1) / per;
   if (w0 == w1) return;
-  float mx = -INFINITY;
-  for (long long s = w0; s <= w1; ++s) mx = fmaxf(mx, a.part_lse[(s + b) * kHeads + h]);
-  float o[16];
+  const int np = (int)(w1 - w0 + 1);
+  const float* lrow = a.part_lse + (w0 + b) * kHeads + h;
+  const PartT* prow = (const PartT*)a.part_o + ((w0 + b) * kHeads + h) * kHeadDim + d0;
+  constexpr int kBatch = 8;
+  float m = -INFINITY, wsum = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < np; s0 += kBatch) {
+    f32x4 part[kBatch];
+    float lw[kBatch];
 #pragma unroll
-  for (int d = 0; d < 16; ++d) o[d] = 0.f;
-  float wsum = 0.f;
-  for (long long s = w0; s <= w1; ++s) {
-    const float wt = fast_exp2(a.part_lse[(s + b) * kHeads + h] - mx);
-    wsum += wt;
-    const float* prow = a.part_o + ((s + b) * kHeads + h) * kHeadDim + d0;
-#pragma unroll
-    for (int d = 0; d < 16; d += 4) {
-      const f32x4 v = *(const f32x4*)(prow + d);
-      o[d] = fmaf(wt, v[0], o[d]);
-      o[d + 1] = fmaf(wt, v[1], o[d + 1]);
-      o[d + 2] = fmaf(wt, v[2], o[d + 2]);
-      o[d + 3] = fmaf(wt, v[3], o[d + 3]);
+    for (int k = 0; k < kBatch; ++k) {
+      const int s = s0 + k < np ? s0 + k : np - 1;
+      part[k] = load4(prow + (long long)s * kHeads * kHeadDim);
+      lw[k] = s0 + k < np ? lrow[(long long)s * kHeads] : -INFINITY;
     }
+    float mb = lw[0];
+#pragma unroll
+    for (int k = 1; k < kBatch; ++k) mb = fmaxf(mb, lw[k]);
+    const float m_new = fmaxf(m, mb);
+    const float sc = fast_exp2(m - m_new);  // 0 on the first batch
+    wsum *= sc;
+    o *= sc;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float wt = fast_exp2(lw[k] - m_new);  // 0 for the padding entries
+      wsum += wt;
+      o += part[k] * wt;
+    }
+    m = m_new;
   }
   const float inv = 1.f / wsum;
 #pragma unroll
-  for (int d = 0; d < 16; ++d) orow[d] = (OutT)(o[d] * inv);
-  if (a.lse != nullptr && (threadIdx.x & 15) == 0)
-    a.lse[(long long)b * kHeads + h] = (mx + fast_log2(wsum)) * kLn2;
+  for (int d = 0; d < 4; ++d) orow[d] = (OutT)(o[d] * inv);
+  if (a.lse != nullptr && lane == 0) a.lse[(long long)b * kHeads + h] = (m + fast_log2(wsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -574,27 +648,27 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
   a.seq_len = p.seq_len;
   a.out = p.out;
   a.lse = p.lse;
-  a.part_o = (float*)p.ws;
+  a.part_o = p.ws;
   a.part_lse = (float*)((char*)p.ws + attn_part_o_bytes(p.B, p.G));
   a.B = p.B;
   a.G = p.G;
   a.score_mul = p.softmax_scale * p.k_scale * kLog2e;
   a.v_mul = p.v_scale;
   const dim3 block(256);
-  const dim3 comb(p.B, 4);
+  const dim3 comb(p.B, 16);
   hipError_t e = hipSuccess;
   switch (p.kind) {
     case AttnKind::F32:
       e = launch(attn_f32_kernel, dim3(p.G), block, stream, a);
-      if (e == hipSuccess) e = launch(attn_combine_kernel<float>, comb, block, stream, a);
+      if (e == hipSuccess) e = launch(attn_combine_kernel<float, float>, comb, block, stream, a);
       break;
     case AttnKind::BF16:
       e = launch(attn_mfma_kernel<false>, dim3(p.G), block, stream, a);
-      if (e == hipSuccess) e = launch(attn_combine_kernel<bf16>, comb, block, stream, a);
+      if (e == hipSuccess) e = launch(attn_combine_kernel<bf16, bf16>, comb, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
       e = launch(attn_mfma_kernel<true>, dim3(p.G), block, stream, a);
-      if (e == hipSuccess) e = launch(attn_combine_kernel<bf16>, comb, block, stream, a);
+      if (e == hipSuccess) e = launch(attn_combine_kernel<bf16, bf16>, comb, block, stream, a);
       break;
   }
   return e;

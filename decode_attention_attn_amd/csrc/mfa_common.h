@@ -78,6 +78,21 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const MFA_LDS i32x2* __restrict__ 
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MFA_LDS i32x2*)p);
 }
 
+// Cross-lane combine of the 4 lanes n, n+16, n+32, n+48 (one value per
+// 16-lane row) with the gfx950 row/half swaps: no LDS round trip.
+__device__ __forceinline__ float max_over_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(r[0]) + __int_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 // Wave-wide reductions over all 64 lanes.
 __device__ __forceinline__ long long wave_sum_ll(long long v) {
 #pragma unroll
