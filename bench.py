@@ -38,12 +38,38 @@ def _kv_bytes(lengths, kv_kind):
     return int(np.asarray(lengths, dtype=np.int64).sum()) * per
 
 
-def _event_time_ms(fn, steps, warmup, stream):
+def _event_time_ms(fn, steps, warmup, stream, graph_calls=0):
+    """Average time per step between HIP events on ``stream``.
+
+    With ``graph_calls`` > 0 the steps are captured ``graph_calls`` at a time
+    into a HIP graph (through torch's graph capture, which records the
+    library's launches on the capture stream) and the graph is replayed, so
+    host-side launch latency does not show in the device time, as in a serving
+    loop. ``fn(i)`` must only enqueue work on the current stream.
+    """
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    if graph_calls > 0:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(graph_calls):
+                fn(i)
+        torch.cuda.synchronize()
+        reps = max(1, steps // graph_calls)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / (reps * graph_calls)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -54,7 +80,7 @@ def _event_time_ms(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps
 
 
-def bench_attn(name, steps, warmup, rotate):
+def bench_attn(name, steps, warmup, rotate, graph=True):
     import torch
 
     from decode_attention_attn_amd import inputs as gen
@@ -65,16 +91,18 @@ def bench_attn(name, steps, warmup, rotate):
     dev = runner.upload_attn(inp)
     ks = [dev["k"]] + [dev["k"].clone() for _ in range(rotate - 1)]
     vs = [dev["v"]] + [dev["v"].clone() for _ in range(rotate - 1)]
-    stream = torch.cuda.current_stream()
-    call = runner.AttnCall(dev, num_workgroups=0, want_lse=False, stream=stream.cuda_stream)
-    ms = _event_time_ms(lambda i: call(ks[i % rotate], vs[i % rotate]), steps, warmup, stream)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        call = runner.AttnCall(dev, num_workgroups=0, want_lse=False, stream=None)
+        ms = _event_time_ms(lambda i: call(ks[i % rotate], vs[i % rotate]), steps, warmup, stream,
+                            graph_calls=4 * rotate if graph else 0)
     B = w.batch
     kv = _kv_bytes(inp["seq_len"], w.kv)
     qo = 2 * B * 64 * 256 * (4 if w.act == "f32" else 2)
     return dict(workload=name, ms=ms, B=B, kv_bytes=kv, alg_bytes=kv + qo, lengths=inp["seq_len"], inp=inp, w=w)
 
 
-def bench_layer(name, steps, warmup):
+def bench_layer(name, steps, warmup, graph=True):
     import torch
 
     from decode_attention_attn_amd import inputs as gen
@@ -83,9 +111,10 @@ def bench_layer(name, steps, warmup):
     w = gen.WORKLOADS[name]
     inp = gen.make_layer(w)
     dev = runner.upload_layer(inp)
-    stream = torch.cuda.current_stream()
-    call = runner.LayerCall(dev, num_workgroups=0, stream=stream.cuda_stream)
-    ms = _event_time_ms(lambda i: call(), steps, warmup, stream)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        call = runner.LayerCall(dev, num_workgroups=0, stream=None)
+        ms = _event_time_ms(lambda i: call(), steps, warmup, stream, graph_calls=8 if graph else 0)
     B = w.batch
     esz = 4 if w.act == "f32" else 2
     kv = _kv_bytes(inp["seq_len"] + 1, w.kv)
@@ -144,6 +173,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the fp8-KV 4K secondary measurement")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step from the host instead of replaying "
+                    "a captured HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -159,9 +190,9 @@ def main():
     import decode_attention_attn_amd.mfa  # noqa: F401  (fails loudly if libmfa.so is missing)
 
     if args.workload.startswith("attn"):
-        res = bench_attn(args.workload, args.steps, args.warmup, args.rotate)
+        res = bench_attn(args.workload, args.steps, args.warmup, args.rotate, graph=not args.no_graph)
     else:
-        res = bench_layer(args.workload, args.steps, args.warmup)
+        res = bench_layer(args.workload, args.steps, args.warmup, graph=not args.no_graph)
     w = res["w"]
     ms = res["ms"]
     gbps = res["kv_bytes"] / (ms * 1e-3) / 1e9
@@ -204,7 +235,7 @@ def main():
         },
     }
     if w.kind == "attn" and not args.no_secondary and args.workload == "attn_bf16_4k":
-        sec = bench_attn("attn_fp8kv_4k", args.steps, args.warmup, args.rotate)
+        sec = bench_attn("attn_fp8kv_4k", args.steps, args.warmup, args.rotate, graph=not args.no_graph)
         s_gbps = sec["kv_bytes"] / (sec["ms"] * 1e-3) / 1e9
         line["secondary"] = {"attn_fp8kv_4k": {
             "ms_per_step": round(sec["ms"], 5), "kv_GBps": round(s_gbps, 2),

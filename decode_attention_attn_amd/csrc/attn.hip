@@ -15,6 +15,10 @@
 //    sequence and the head of the next, so ragged lengths never leave CUs
 //    idle. A sequence cut into several pieces is merged afterwards by a
 //    log-sum-exp combine; a sequence inside one piece is written directly.
+//    A split piece stores its normalised partial in bf16 in the MFMA register
+//    layout (eight 1 KB contiguous stores per wave), and the workgroup holding
+//    a sequence's first piece records where its pieces are, so the combine
+//    kernel goes straight to its loads.
 //  * Data path. Tiles of 32 KB (32 bf16 rows or 64 fp8 rows of K, then of V)
 //    go HBM -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4: each lane
 //    moves 16 B, a wave 1 KB) into a 4-stage ring, three tiles ahead of the
@@ -52,6 +56,7 @@ struct AttnArgs {
   float* lse;
   void* part_o;     // [G + B][64][256] normalized partial outputs (bf16 for the MFMA kernels, fp32 otherwise)
   float* part_lse;  // [G + B][64] fp32, base-2 log-sum-exp of each partial
+  int* meta;        // [B][2]: first partial slot and piece count of each sequence (0 pieces: written directly)
   int B;
   int G;
   float score_mul;  // softmax_scale * k_scale * log2(e)
@@ -73,59 +78,11 @@ __device__ __forceinline__ long long piece_len(long long total, int G) {
 // each sequence over all XCDs balances their memory paths.)
 __device__ __forceinline__ int piece_index(int /*G*/) { return blockIdx.x; }
 
-// Total length, plus the sequence containing global position r0 and its start
-// (only when 0 <= r0 < total). One pass over seq_len for B <= 256.
-__device__ __forceinline__ void scan_lengths(const int32_t* len, int B, int G, int wgi, int lane,
-                                             long long& total, long long& per, long long& r0, int& b_out,
-                                             long long& start_out) {
-  constexpr int kCached = 4;
-  long long vals[kCached];
-  long long s = 0;
-#pragma unroll
-  for (int c = 0; c < kCached; ++c) {
-    const int i = 64 * c + lane;
-    vals[c] = i < B ? (long long)len[i] : 0;
-    s += vals[c];
-  }
-  for (int i = 64 * kCached + lane; i < B; i += 64) s += len[i];
-  total = uniform(wave_sum_ll(s));
-  per = piece_len(total, G);
-  r0 = (long long)wgi * per;
-  b_out = B - 1;
-  start_out = 0;
-  if (r0 >= total) return;
-  long long base = 0;
-  for (int c0 = 0, c = 0; c0 < B; c0 += 64, ++c) {
-    const int idx = c0 + lane;
-    long long v;
-    if (c < kCached) {
-      v = vals[0];
-#pragma unroll
-      for (int k = 1; k < kCached; ++k) v = (c == k) ? vals[k] : v;
-    } else {
-      v = idx < B ? (long long)len[idx] : 0;
-    }
-    long long incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    const unsigned long long hit = __ballot(idx < B && base + incl > r0);
-    if (hit) {
-      const int first = __ffsll((long long)hit) - 1;
-      b_out = uniform(c0 + first);
-      start_out = uniform(base + __shfl(incl, first) - __shfl(v, first));
-      return;
-    }
-    base += __shfl(incl, 63);
-  }
-}
-
 // Walks one workgroup's piece tile by tile (wave-uniform state).
 template <int kRows>
 struct Cursor {
   long long gpos, r1;            // next global position, end of the workgroup's piece
+  long long per;                 // piece length (rows per workgroup)
   long long seq_start, seq_end;  // global range of the current sequence
   long long off;                 // cache row of the sequence's first key
   int b;
@@ -154,19 +111,51 @@ struct Cursor {
   }
 };
 
+// A workgroup's start: total length, piece length, and the sequence holding
+// its first position r0 = wgi * per (with that sequence's start and cache
+// offset). Kept short: it runs before the first tile load, when the code is
+// not yet in the instruction cache and every fetch of it queues behind the
+// tile loads of the workgroups that got going first. The first 64 sequences
+// stay in registers; more are re-read chunk by chunk.
 template <int kRows>
 __device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane, Cursor<kRows>& c) {
-  long long total, per, r0, start;
-  int b;
-  scan_lengths(a.seq_len, a.B, a.G, wgi, lane, total, per, r0, b, start);
+  const int B = a.B;
+  const int ic = lane < B ? lane : B - 1;
+  const long long v0 = lane < B ? (long long)a.seq_len[ic] : 0;
+  const long long o0 = a.seq_off[ic];
+  long long sum = v0;
+  for (int i = 64 + lane; i < B; i += 64) sum += a.seq_len[i];
+  const long long total = uniform(wave_sum_ll(sum));
+  const long long per = piece_len(total, a.G);
+  const long long r0 = (long long)wgi * per;
   if (r0 >= total) return false;
-  c.r1 = r0 + per < total ? r0 + per : total;
-  c.gpos = r0;
-  c.b = b;
-  c.seq_start = start;
-  c.seq_end = start + load_scalar(a.seq_len, b);
-  c.off = load_scalar(a.seq_off, b);
-  return true;
+  long long base = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int i = c0 + lane;
+    const long long v = c0 == 0 ? v0 : (i < B ? (long long)a.seq_len[i] : 0);
+    long long incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const unsigned long long hit = __ballot(i < B && base + incl > r0);
+    if (hit) {
+      const int first = __ffsll((long long)hit) - 1;
+      const int b = uniform(c0 + first);
+      const long long start = uniform(base + __shfl(incl - v, first));
+      c.r1 = r0 + per < total ? r0 + per : total;
+      c.per = per;
+      c.gpos = r0;
+      c.b = b;
+      c.seq_start = start;
+      c.seq_end = start + uniform(__shfl(v, first));
+      c.off = c0 == 0 ? uniform(__shfl(o0, first)) : load_scalar(a.seq_off, b);
+      return true;
+    }
+    base += __shfl(incl, 63);
+  }
+  return false;  // not reached: r0 < total
 }
 
 // ---------------------------------------------------------------------------
@@ -425,6 +414,12 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
       const float lse2 = m_run + fast_log2(lt);
       const int h = 16 * w + n;
       const long long L = cons.seq_end - cons.seq_start;
+      if (piece_lo == 0 && threadIdx.x == 0) {
+        // this workgroup holds the sequence's first piece: tell the combine
+        // where its pieces are (w0 = wgi; none when it is whole here)
+        const int np = hi == L ? 0 : (int)((cons.seq_start + L - 1) / cons.per - wgi + 1);
+        *(i32x2*)(a.meta + 2 * cons.b) = i32x2{wgi + cons.b, np};
+      }
       if (piece_lo == 0 && hi == L) {
         bf16* orow = (bf16*)a.out + ((long long)cons.b * kHeads + h) * kHeadDim + 4 * g;
 #pragma unroll
@@ -435,15 +430,17 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
         }
         if (a.lse != nullptr && g == 0) a.lse[(long long)cons.b * kHeads + h] = lse2 * kLn2;
       } else {
-        // partial outputs in bf16: half the bytes of the round trip through
-        // memory; the merge weights (lse) stay fp32
+        // partial outputs in bf16 (half the bytes of the round trip through
+        // memory; the merge weights stay fp32), in the register layout: one
+        // 1 KB contiguous store per wave and channel-block pair (the combine
+        // knows the map)
         const long long slot = (long long)wgi + cons.b;
-        bf16* prow = (bf16*)a.part_o + (slot * kHeads + h) * kHeadDim + 4 * g;
+        bf16x8* prow = (bf16x8*)a.part_o + slot * (kHeads * kHeadDim / 8);
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
-          const bf16x4 o = {(bf16)(acc[db][0] * inv), (bf16)(acc[db][1] * inv), (bf16)(acc[db][2] * inv),
-                            (bf16)(acc[db][3] * inv)};
-          *(bf16x4*)(prow + 16 * db) = o;
+        for (int dp = 0; dp < 8; ++dp) {
+          const f32x4 v0 = acc[2 * dp] * inv, v1 = acc[2 * dp + 1] * inv;
+          prow[(w * 8 + dp) * 64 + lane] = bf16x8{(bf16)v0[0], (bf16)v0[1], (bf16)v0[2], (bf16)v0[3],
+                                                  (bf16)v1[0], (bf16)v1[1], (bf16)v1[2], (bf16)v1[3]};
         }
         if (g == 0) a.part_lse[slot * kHeads + h] = lse2;
       }
@@ -546,6 +543,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       const float inv = a.v_mul / l_run;
       const float lse2 = m_run + fast_log2(l_run);
       const long long L = cons.seq_end - cons.seq_start;
+      if (piece_lo == 0 && threadIdx.x == 0) {
+        const int np = hi == L ? 0 : (int)((cons.seq_start + L - 1) / cons.per - wgi + 1);
+        *(i32x2*)(a.meta + 2 * cons.b) = i32x2{wgi + cons.b, np};
+      }
       float* dst;
       if (piece_lo == 0 && hi == L) {
         dst = (float*)a.out + ((long long)cons.b * kHeads + h) * kHeadDim + 64 * g;
@@ -565,46 +566,32 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the pieces of each split sequence. Grid (B, 16): block
-// (b, hq) merges heads 4hq..4hq+3; thread t owns head 4hq + t/64 and channels
-// 4*(t%64)..+3. Sequences inside one piece were written by the attention
-// kernel and are skipped; empty sequences get out = 0, lse = -inf. Partials
-// are read 8 at a time and merged with a running max (one pass).
-__device__ __forceinline__ f32x4 load4(const float* p) { return *(const f32x4*)p; }
-__device__ __forceinline__ f32x4 load4(const bf16* p) {
-  const bf16x4 v = *(const bf16x4*)p;
-  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
+// Log-sum-exp merge of the pieces of each split sequence (the combine rule of
+// split-KV decoding: weights exp(lse_s - lse), lse = log sum exp lse_s).
+// Sequences inside one piece were written by the attention kernel and are
+// skipped; empty sequences get out = 0, lse = -inf. Partials are read 8 at a
+// time and merged with a running max (one pass).
 
-template <typename OutT, typename PartT>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+// fp32 partials in [slot][head][channel] layout. Grid (B, 16): block (b, hq)
+// merges heads 4hq..4hq+3; thread t owns head 4hq + t/64, channels 4(t%64)..+3.
+__global__ __launch_bounds__(256) void attn_combine_f32_kernel(AttnArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
   const int d0 = 4 * lane;
   const long long L = load_scalar(a.seq_len, b);
-  OutT* orow = (OutT*)a.out + ((long long)b * kHeads + h) * kHeadDim + d0;
+  float* orow = (float*)a.out + ((long long)b * kHeads + h) * kHeadDim + d0;
   if (L == 0) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) orow[d] = (OutT)0.f;
+    *(f32x4*)orow = f32x4{0.f, 0.f, 0.f, 0.f};
     if (a.lse != nullptr && lane == 0) a.lse[(long long)b * kHeads + h] = -INFINITY;
     return;
   }
-  // total length and this sequence's start in one pass over seq_len
-  long long s_all = 0, s_before = 0;
-  for (int i = lane; i < a.B; i += 64) {
-    const long long v = a.seq_len[i];
-    s_all += v;
-    s_before += i < b ? v : 0;
-  }
-  const long long total = uniform(wave_sum_ll(s_all));
-  const long long start = uniform(wave_sum_ll(s_before));
-  const long long per = piece_len(total, a.G);
-  const long long w0 = start / per, w1 = (start + L - 1) / per;
-  if (w0 == w1) return;
-  const int np = (int)(w1 - w0 + 1);
-  const float* lrow = a.part_lse + (w0 + b) * kHeads + h;
-  const PartT* prow = (const PartT*)a.part_o + ((w0 + b) * kHeads + h) * kHeadDim + d0;
+  // written by the attention kernel for every non-empty sequence
+  const int np = load_scalar(a.meta, 2LL * b + 1);
+  if (np == 0) return;
+  const long long slot0 = load_scalar(a.meta, 2LL * b);
+  const float* lrow = a.part_lse + slot0 * kHeads + h;
+  const float* prow = (const float*)a.part_o + (slot0 * kHeads + h) * kHeadDim + d0;
   constexpr int kBatch = 8;
   float m = -INFINITY, wsum = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -614,7 +601,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int s = s0 + k < np ? s0 + k : np - 1;
-      part[k] = load4(prow + (long long)s * kHeads * kHeadDim);
+      part[k] = *(const f32x4*)(prow + (long long)s * kHeads * kHeadDim);
       lw[k] = s0 + k < np ? lrow[(long long)s * kHeads] : -INFINITY;
     }
     float mb = lw[0];
@@ -632,10 +619,70 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     }
     m = m_new;
   }
-  const float inv = 1.f / wsum;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) orow[d] = (OutT)(o[d] * inv);
+  *(f32x4*)orow = o * (1.f / wsum);
   if (a.lse != nullptr && lane == 0) a.lse[(long long)b * kHeads + h] = (m + fast_log2(wsum)) * kLn2;
+}
+
+// bf16 partials in the MFMA kernel's register layout: 16-byte chunk
+// c = (w*8 + dp)*64 + lane of a slot holds head 16w + (lane%16), channels
+// 32dp + 4(lane/16) + {0..3} and the same + 16. Grid (B, 8): thread c of the
+// sequence merges chunk c of every partial.
+__global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
+  const int b = blockIdx.x;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int lane = c & 63, dp = (c >> 6) & 7, w = c >> 9;
+  const int n = lane & 15, g = lane >> 4;
+  const int h = 16 * w + n;
+  const long long L = load_scalar(a.seq_len, b);
+  bf16* orow = (bf16*)a.out + ((long long)b * kHeads + h) * kHeadDim + 32 * dp + 4 * g;
+  const bool lse_owner = a.lse != nullptr && dp == 0 && g == 0;
+  if (L == 0) {
+    *(bf16x4*)orow = bf16x4{};
+    *(bf16x4*)(orow + 16) = bf16x4{};
+    if (lse_owner) a.lse[(long long)b * kHeads + h] = -INFINITY;
+    return;
+  }
+  // written by the attention kernel for every non-empty sequence
+  const int np = load_scalar(a.meta, 2LL * b + 1);
+  if (np == 0) return;
+  const long long slot0 = load_scalar(a.meta, 2LL * b);
+  const float* lrow = a.part_lse + slot0 * kHeads + h;
+  const bf16x8* prow = (const bf16x8*)a.part_o + slot0 * (kHeads * kHeadDim / 8) + c;
+  constexpr int kBatch = 8;
+  float m = -INFINITY, wsum = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < np; s0 += kBatch) {
+    bf16x8 part[kBatch];
+    float lw[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int s = s0 + k < np ? s0 + k : np - 1;
+      part[k] = prow[(long long)s * (kHeads * kHeadDim / 8)];
+      lw[k] = s0 + k < np ? lrow[(long long)s * kHeads] : -INFINITY;
+    }
+    float mb = lw[0];
+#pragma unroll
+    for (int k = 1; k < kBatch; ++k) mb = fmaxf(mb, lw[k]);
+    const float m_new = fmaxf(m, mb);
+    const float sc = fast_exp2(m - m_new);  // 0 on the first batch
+    wsum *= sc;
+    o0 *= sc;
+    o1 *= sc;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float wt = fast_exp2(lw[k] - m_new);  // 0 for the padding entries
+      wsum += wt;
+      o0 += f32x4{(float)part[k][0], (float)part[k][1], (float)part[k][2], (float)part[k][3]} * wt;
+      o1 += f32x4{(float)part[k][4], (float)part[k][5], (float)part[k][6], (float)part[k][7]} * wt;
+    }
+    m = m_new;
+  }
+  const float inv = 1.f / wsum;
+  o0 *= inv;
+  o1 *= inv;
+  *(bf16x4*)orow = bf16x4{(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3]};
+  *(bf16x4*)(orow + 16) = bf16x4{(bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
+  if (lse_owner) a.lse[(long long)b * kHeads + h] = (m + fast_log2(wsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -650,25 +697,27 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
   a.lse = p.lse;
   a.part_o = p.ws;
   a.part_lse = (float*)((char*)p.ws + attn_part_o_bytes(p.B, p.G));
+  a.meta = (int*)((char*)p.ws + attn_meta_offset(p.B, p.G));
   a.B = p.B;
   a.G = p.G;
   a.score_mul = p.softmax_scale * p.k_scale * kLog2e;
   a.v_mul = p.v_scale;
   const dim3 block(256);
-  const dim3 comb(p.B, 16);
+  const dim3 comb_f32(p.B, 16);
+  const dim3 comb_mfma(p.B, 8);
   hipError_t e = hipSuccess;
   switch (p.kind) {
     case AttnKind::F32:
       e = launch(attn_f32_kernel, dim3(p.G), block, stream, a);
-      if (e == hipSuccess) e = launch(attn_combine_kernel<float, float>, comb, block, stream, a);
+      if (e == hipSuccess) e = launch(attn_combine_f32_kernel, comb_f32, block, stream, a);
       break;
     case AttnKind::BF16:
       e = launch(attn_mfma_kernel<false>, dim3(p.G), block, stream, a);
-      if (e == hipSuccess) e = launch(attn_combine_kernel<bf16, bf16>, comb, block, stream, a);
+      if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
       e = launch(attn_mfma_kernel<true>, dim3(p.G), block, stream, a);
-      if (e == hipSuccess) e = launch(attn_combine_kernel<bf16, bf16>, comb, block, stream, a);
+      if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
   }
   return e;

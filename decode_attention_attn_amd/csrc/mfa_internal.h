@@ -43,11 +43,12 @@ struct AttnLaunch {
   float softmax_scale, k_scale, v_scale;
 };
 
-// Partials: [G + B][64][256] fp32 outputs then [G + B][64] fp32 lse.
+// Workspace: partial outputs [G + B][64][256] (fp32-sized; bf16 partials use
+// half), partial lse [G + B][64] fp32, then per-sequence combine metadata
+// [B] x {first slot, piece count}.
 inline size_t attn_part_o_bytes(int B, int G) { return (size_t)(G + B) * 64 * 256 * sizeof(float); }
-inline size_t attn_ws_bytes(int B, int G) {
-  return attn_part_o_bytes(B, G) + (size_t)(G + B) * 64 * sizeof(float);
-}
+inline size_t attn_meta_offset(int B, int G) { return attn_part_o_bytes(B, G) + (size_t)(G + B) * 64 * sizeof(float); }
+inline size_t attn_ws_bytes(int B, int G) { return attn_meta_offset(B, G) + (size_t)B * 2 * sizeof(int); }
 
 hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream);
 

@@ -37,7 +37,7 @@ def test_version_and_status_strings():
 
 def test_workspace_sizes():
     B, G = 32, 256
-    assert mfa.mfa_decode_attn_workspace_size(B, G) == (G + B) * 64 * 256 * 4 + (G + B) * 64 * 4
+    assert mfa.mfa_decode_attn_workspace_size(B, G) == (G + B) * 64 * 256 * 4 + (G + B) * 64 * 4 + B * 8
     assert mfa.mfa_decode_attn_workspace_size(0, G) == 0
     assert mfa.mfa_decode_attn_workspace_size(B, -1) == 0
     for fn in (mfa.mfa_qproj_workspace_size, mfa.mfa_kv_append_workspace_size):
