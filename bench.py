@@ -29,6 +29,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MFA decode attn: KV-cache HBM GB/s (% of peak) + decode tokens/s at 4K ctx"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+# Sources the attention kernels are built from: HBM traffic measured with
+# rocprofv3 counters is reported only while they are unchanged.
+KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/attn.hip", "decode_attention_attn_amd/csrc/mfa_common.h",
+                  "decode_attention_attn_amd/csrc/mfa_internal.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per call (FETCH_SIZE + WRITE_SIZE, copy-calibrated) recorded
+    for this workload, or None when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("workloads", {}).get(workload)
+    if ent is None or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_call")
 
 
 def _kv_bytes(lengths, kv_kind):
@@ -175,6 +204,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the fp8-KV 4K secondary measurement")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host instead of replaying "
                     "a captured HIP graph")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first copy this many MiB device-to-device three times (a plain copy kernel of known size, "
+                    "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -189,6 +221,15 @@ def main():
         sys.exit(2)
     import decode_attention_attn_amd.mfa  # noqa: F401  (fails loudly if libmfa.so is missing)
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     if args.workload.startswith("attn"):
         res = bench_attn(args.workload, args.steps, args.warmup, args.rotate, graph=not args.no_graph)
     else:
@@ -197,6 +238,7 @@ def main():
     ms = res["ms"]
     gbps = res["kv_bytes"] / (ms * 1e-3) / 1e9
     achieved = res["alg_bytes"] / (ms * 1e-3) / 1e9
+    hbm_bytes = measured_traffic(w.name)
     line = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -228,9 +270,12 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "kernel": "attn_mfma_kernel + attn_combine_kernel (whole call, HIP events)"
-            if w.kind == "attn" else "whole layer (HIP events)",
+            # HBM bytes per call from rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-calibrated), as a rate over the
+            # same call time as "achieved"; null when the kernel sources changed since the counters were taken
+            "traffic": None if hbm_bytes is None else round(hbm_bytes / (ms * 1e-3) / 1e9, 2),
+            "traffic_bytes_per_launch": hbm_bytes,
+            "kernel": "mfa_decode_attn call = attn_mfma_kernel + attn_combine_mfma_kernel (HIP events on the "
+            "call's stream)" if w.kind == "attn" else "whole layer (HIP events)",
             "alg_bytes_per_launch": res["alg_bytes"],
         },
     }
