@@ -73,10 +73,16 @@ __device__ __forceinline__ long long piece_len(long long total, int G) {
   return (per + kPieceAlign - 1) / kPieceAlign * kPieceAlign;
 }
 
-// Workgroup w takes piece w. (Placing the pieces of a sequence on one XCD, to
-// share its L2, measured no faster: the cache stream dominates and spreading
-// each sequence over all XCDs balances their memory paths.)
-__device__ __forceinline__ int piece_index(int /*G*/) { return blockIdx.x; }
+// Which piece a workgroup takes. Workgroups are dealt round-robin to the 8
+// XCDs (workgroup i runs on XCD i % 8), so piece (i % 8) * (G / 8) + i / 8
+// gives each XCD a contiguous run of pieces: the pieces of a sequence share
+// one L2, so its q is fetched from memory once per XCD rather than once per
+// piece, and neighbouring pieces finish together. Placement only affects
+// speed; any bijection of the workgroup indices is correct.
+__device__ __forceinline__ int piece_index(int G) {
+  const int i = blockIdx.x;
+  return (G & 7) == 0 ? (i & 7) * (G >> 3) + (i >> 3) : i;
+}
 
 // Walks one workgroup's piece tile by tile (wave-uniform state).
 template <int kRows>

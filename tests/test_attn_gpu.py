@@ -87,6 +87,45 @@ def test_empty_sequences_give_zero_and_minus_inf():
     assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2])) and np.all(np.isfinite(lse[1]))
 
 
+@pytest.mark.parametrize("G", [3, 0])
+def test_empty_sequences_beyond_the_first_64(G):
+    # empties among the first 64 sequences and after them take different paths
+    r = _runner()
+    lengths = np.full(70, 5, dtype=np.int32)
+    lengths[[0, 2, 63, 64, 69]] = 0
+    lengths[[1, 65]] = 300
+    print(f"[case] 70 sequences with empties, G={G}", flush=True)
+    inp = _make("bf16", lengths=lengths)
+    out, lse, _ = r.decode_attn(inp, num_workgroups=G)
+    o_ref, l_ref = _oracle(inp)
+    check(f"out empties G={G}", r.to_f64(out), o_ref, 2e-2, 1e-2)
+    check_lse(f"lse empties G={G}", r.to_f64(lse), l_ref, 2e-3)
+
+
+def test_workspace_reuse_across_batch_sizes():
+    # one workspace, calls of different sizes in turn: results must not
+    # depend on what ran before in it, and repeat bit for bit
+    r = _runner()
+    print("[case] workspace reuse across batch sizes", flush=True)
+    inp_a = _make("bf16", lengths=[3000, 17, 1500, 4096])
+    inp_b = _make("bf16", lengths=LENGTHS, seed=1)
+    call_a = r.AttnCall(r.upload_attn(inp_a))
+    call_b = r.AttnCall(r.upload_attn(inp_b))
+    assert call_b.ws.numel() >= call_a.ws.numel()
+    call_a.ws = call_b.ws
+    outs = []
+    for call in (call_a, call_b, call_a, call_b):
+        o, l = call()
+        torch.cuda.synchronize()
+        outs.append((r.to_f64(o), r.to_f64(l)))
+    for (o, l), inp in zip(outs[:2], (inp_a, inp_b)):
+        o_ref, l_ref = _oracle(inp)
+        check("reused workspace out", o, o_ref, 2e-2, 1e-2)
+        check_lse("reused workspace lse", l, l_ref, 2e-3)
+    for i in (0, 1):
+        assert np.array_equal(outs[i][0], outs[i + 2][0]) and np.array_equal(outs[i][1], outs[i + 2][1])
+
+
 def test_splits_agree_and_repeat_bitwise():
     r = _runner()
     print("[case] split agreement / determinism", flush=True)
