@@ -216,34 +216,101 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
   }
 }
 
+// q of head 16w + n, the channels this lane's k-slot group g supplies to the
+// score product: bf16 step j covers channels 32j + 8g..+7; fp8 step kk (k = 128)
+// covers channels 128kk + 32g..+31 (qf[4kk + m] holds 128kk + 32g + 8m..+7).
 template <bool FP8>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int w, int n, int g, bf16x8 (&qf)[8]) {
   const bf16* qrow = (const bf16*)a.q + ((long long)b * kHeads + 16 * w + n) * kHeadDim;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    // k-slot group g of step j <-> the same 8 channels the K operand reads
-    const int d0 = FP8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g);
+    const int d0 = FP8 ? (128 * (j >> 2) + 32 * g + 8 * (j & 3)) : (32 * j + 8 * g);
     qf[j] = *(const bf16x8*)(qrow + d0);
   }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 cache, score product: the cache's K bytes feed the gfx950 fp8 MFMA
+// (v_mfma_f32_16x16x128_f8f6f4, e4m3 operands, twice the bf16 rate) without
+// any widening. q is carried as two e4m3 numbers, q ~ 2^e (hi + lo / 16) with
+// hi = fp8(q 2^-e) and lo = fp8(16 (q 2^-e - hi)), where 2^e puts the head's
+// largest |q| in [128, 256); the pair keeps about 8 significant bits (as bf16
+// does) and two k = 128 fp8 products cost what one bf16 product of the same
+// width does. (A single fp8 q would keep 4 bits.)
+struct Q8 {
+  i32x8 hi[2], lo[2];  // score step kk: channels 128kk + 32g..+31, byte i <-> channel 128kk + 32g + i
+  float mul;           // 2^e
+};
+
+// 32 floats -> 32 e4m3 bytes (round to nearest even), byte i <- v[i].
+__device__ __forceinline__ i32x8 pack_fp8x32(const float (&v)[32]) {
+  i32x8 r;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d], v[4 * d + 1], 0, false);
+    r[d] = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d + 2], v[4 * d + 3], x, true);
+  }
+  return r;
+}
+
+__device__ __forceinline__ void split_q8(const bf16x8 (&qf)[8], Q8& q) {
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf((float)qf[j][i]));
+  mx = max_over_rows(mx);  // the 4 lanes of a head hold all its channels
+  int e = 0;
+  if (mx > 0.f) {
+    int ex;
+    frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+    e = ex - 8;
+  }
+  q.mul = ldexpf(1.f, e);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float v[32], r[32];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[8 * m + i] = ldexpf((float)qf[4 * kk + m][i], -e);
+    q.hi[kk] = pack_fp8x32(v);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(q.hi[kk][d], false);
+      const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(q.hi[kk][d], true);
+      r[4 * d] = (v[4 * d] - b0[0]) * 16.f;
+      r[4 * d + 1] = (v[4 * d + 1] - b0[1]) * 16.f;
+      r[4 * d + 2] = (v[4 * d + 2] - b1[0]) * 16.f;
+      r[4 * d + 3] = (v[4 * d + 3] - b1[1]) * 16.f;
+    }
+    q.lo[kk] = pack_fp8x32(r);
+  }
+}
+
+// fp8 K operand of score step kk for rows 16pb..16pb+15 of the 32-row block
+// at ks: row 16pb + n, channels 128kk + 32g..+31 = chunks 8kk + 2g and
+// 8kk + 2g + 1, stored at slots chunk ^ n.
+__device__ __forceinline__ i32x8 read_k8(const char* ks, int n, int g, int pb, int kk) {
+  const char* row = ks + (16 * pb + n) * 256;
+  const int c = 8 * kk + 2 * g;
+  const u32x4 a = *(const MFA_LDS u32x4*)(row + ((c ^ n) << 4));
+  const u32x4 b = *(const MFA_LDS u32x4*)(row + (((c + 1) ^ n) << 4));
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, const f32x4& c) {
+  // e4m3 x e4m3 (format code 0), unit scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // K operand (A of S^T = K Q^T) for rows 16pb..16pb+15 of the 32-row block at
 // ks: kf[j] holds the 8 channels of k-slot group g at step j for row 16pb + n.
 template <bool FP8>
 __device__ __forceinline__ void read_k(const char* ks, int n, int g, bf16x8 (&kf)[8], int pb) {
-  if constexpr (!FP8) {
+  static_assert(!FP8, "the fp8 score product reads K with read_k8");
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kf[j] = *(const MFA_LDS bf16x8*)(ks + (16 * pb + n) * 512 + (((4 * j + g) ^ n) << 4));
-  } else {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const u32x4 r = *(const MFA_LDS u32x4*)(ks + (16 * pb + n) * 256 + (((4 * jj + g) ^ n) << 4));
-      fp8x4_to_bf16(r[0], kf[2 * jj], 0);
-      fp8x4_to_bf16(r[1], kf[2 * jj], 4);
-      fp8x4_to_bf16(r[2], kf[2 * jj + 1], 0);
-      fp8x4_to_bf16(r[3], kf[2 * jj + 1], 4);
-    }
-  }
+  for (int j = 0; j < 8; ++j) kf[j] = *(const MFA_LDS bf16x8*)(ks + (16 * pb + n) * 512 + (((4 * j + g) ^ n) << 4));
 }
 
 // V^T operand (A of O^T = V^T P^T): the fragment of channel block db holds,
@@ -291,22 +358,44 @@ struct VReader {
 // One 32-row block: scores, online softmax update, PV accumulate.
 template <bool FP8>
 __device__ __forceinline__ void attend_block(const char* ks, const char* vs, int nvalid, int n, int g,
-                                             const VReader<FP8>& vr, const bf16x8 (&qf)[8], float score_mul,
-                                             float& m_run, float& l_run, f32x4 (&acc)[16]) {
+                                             const VReader<FP8>& vr, const bf16x8 (&qf)[8], const Q8& q8,
+                                             float score_mul, float& m_run, float& l_run, f32x4 (&acc)[16]) {
   // K fragments first, then the score MFMAs interleaved with the V reads (V
   // does not depend on the scores), so that LDS latency overlaps matrix work.
-  bf16x8 kf0[8], kf1[8];
-  read_k<FP8>(ks, n, g, kf0, 0);
-  read_k<FP8>(ks, n, g, kf1, 1);
-  __builtin_amdgcn_sched_barrier(0);
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   bf16x8 vf[16];
+  if constexpr (!FP8) {
+    bf16x8 kf0[8], kf1[8];
+    read_k<FP8>(ks, n, g, kf0, 0);
+    read_k<FP8>(ks, n, g, kf1, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[j], qf[j], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[j], qf[j], s1, 0, 0, 0);
-    vf[2 * j] = vr.read(vs, 2 * j);
-    vf[2 * j + 1] = vr.read(vs, 2 * j + 1);
+    for (int j = 0; j < 8; ++j) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[j], qf[j], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[j], qf[j], s1, 0, 0, 0);
+      vf[2 * j] = vr.read(vs, 2 * j);
+      vf[2 * j + 1] = vr.read(vs, 2 * j + 1);
+    }
+  } else {
+    i32x8 k00 = read_k8(ks, n, g, 0, 0), k01 = read_k8(ks, n, g, 0, 1);
+    i32x8 k10 = read_k8(ks, n, g, 1, 0), k11 = read_k8(ks, n, g, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 l0 = s0, l1 = s0;  // lo parts
+    s0 = mfma_fp8_k128(k00, q8.hi[0], s0);
+    s1 = mfma_fp8_k128(k10, q8.hi[0], s1);
+    l0 = mfma_fp8_k128(k00, q8.lo[0], l0);
+    l1 = mfma_fp8_k128(k10, q8.lo[0], l1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vf[db] = vr.read(vs, db);
+    s0 = mfma_fp8_k128(k01, q8.hi[1], s0);
+    s1 = mfma_fp8_k128(k11, q8.hi[1], s1);
+    l0 = mfma_fp8_k128(k01, q8.lo[1], l0);
+    l1 = mfma_fp8_k128(k11, q8.lo[1], l1);
+#pragma unroll
+    for (int db = 8; db < 16; ++db) vf[db] = vr.read(vs, db);
+    s0 += l0 * 0.0625f;
+    s1 += l1 * 0.0625f;
+    score_mul *= q8.mul;
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -371,6 +460,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   // wait would leave Q looking pending to the compiler, which would then
   // drain the ring before every score product in the loop.
   wait_vmcnt<0>();
+  Q8 q8;  // fp8 cache: q as hi/lo e4m3 pairs
+  if constexpr (FP8) split_q8(qf, q8);
 
   f32x4 acc[16];
 #pragma unroll
@@ -386,6 +477,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
       // Later pieces of the workgroup: a full drain for their Q (rare).
       load_q<FP8>(a, cons.b, w, n, g, qf);
       wait_vmcnt<0>();
+      if constexpr (FP8) split_q8(qf, q8);
       m_run = -INFINITY;  // the first block rescales acc by exp2(-inf) = 0
       piece_lo = cons.gpos - cons.seq_start;
       fresh = false;
@@ -405,11 +497,11 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     long long lo, hi;
     cons.tile(lo, hi);
     const int nvalid = (int)(hi - lo);
-    attend_block<FP8>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
+    attend_block<FP8>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, q8, a.score_mul, m_run, l_run, acc);
     if constexpr (FP8) {
       if (nvalid > 32)
         attend_block<FP8>(stage + 32 * C::kRowBytes, stage + C::kHalfBytes + 32 * C::kRowBytes, nvalid - 32, n, g,
-                          vr, qf, a.score_mul, m_run, l_run, acc);
+                          vr, qf, q8, a.score_mul, m_run, l_run, acc);
     }
 
     const long long pe = cons.part_end() - cons.seq_start;
