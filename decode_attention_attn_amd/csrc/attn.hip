@@ -216,16 +216,30 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
   }
 }
 
+// q of sequence b ([64 heads][256] bf16, 32 KB) goes HBM -> LDS by DMA like
+// the cache tiles: it is then tracked by the same wait counts, so the
+// prologue can wait for q and the first tile only, and the compiler never
+// sees q as a pending register load.
+__device__ __forceinline__ void issue_q(const AttnArgs& a, int b, char* qs, int w, int lane) {
+  const char* src = (const char*)a.q + (long long)b * (kHeads * kHeadDim * 2);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int blk = w * 8 + jj;  // 32 blocks of 1 KB
+    __builtin_amdgcn_global_load_lds((const void*)(src + blk * 1024 + lane * 16), (MFA_LDS void*)(qs + blk * 1024),
+                                     16, 0, 0);
+  }
+}
+
 // q of head 16w + n, the channels this lane's k-slot group g supplies to the
 // score product: bf16 step j covers channels 32j + 8g..+7; fp8 step kk (k = 128)
 // covers channels 128kk + 32g..+31 (qf[4kk + m] holds 128kk + 32g + 8m..+7).
 template <bool FP8>
-__device__ __forceinline__ void load_q(const AttnArgs& a, int b, int w, int n, int g, bf16x8 (&qf)[8]) {
-  const bf16* qrow = (const bf16*)a.q + ((long long)b * kHeads + 16 * w + n) * kHeadDim;
+__device__ __forceinline__ void read_q(const char* qs, int w, int n, int g, bf16x8 (&qf)[8]) {
+  const char* row = qs + (16 * w + n) * (kHeadDim * 2);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int d0 = FP8 ? (128 * (j >> 2) + 32 * g + 8 * (j & 3)) : (32 * j + 8 * g);
-    qf[j] = *(const bf16x8*)(qrow + d0);
+    qf[j] = lds_read_b128((const MFA_LDS bf16x8*)(row + 2 * d0));
   }
 }
 
@@ -433,9 +447,11 @@ __device__ __forceinline__ void attend_block(const char* ks, const char* vs, int
 template <bool FP8>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   using C = Cfg<FP8>;
-  __shared__ __attribute__((aligned(1024))) char ring[C::kStages * C::kTileBytes];
+  // the 4-stage tile ring, then q (32 KB): 160 KB of LDS
+  __shared__ __attribute__((aligned(1024))) char ring[C::kStages * C::kTileBytes + kHeads * kHeadDim * 2];
+  char* const qs = ring + C::kStages * C::kTileBytes;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = uniform((int)(threadIdx.x >> 6));
   const int n = lane & 15;
   const int g = lane >> 4;
   const int wgi = piece_index(a.G);
@@ -444,9 +460,8 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   if (!init_cursor(a, wgi, lane, prod)) return;
   Cursor<C::kRows> cons = prod;
 
-  // Q of the first piece goes out together with the first tile DMAs.
-  bf16x8 qf[8];
-  load_q<FP8>(a, cons.b, w, n, g, qf);
+  // q of the first piece goes out ahead of the first tile DMAs.
+  issue_q(a, cons.b, qs, w, lane);
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s) {
@@ -456,10 +471,18 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
       ++issued;
     }
   }
-  // A full wait here (Q and the prologue tiles arrive together): a partial
-  // wait would leave Q looking pending to the compiler, which would then
-  // drain the ring before every score product in the loop.
-  wait_vmcnt<0>();
+  // q and tile 0 have landed once at most the later prologue tiles are in
+  // flight (DMAs complete in issue order); the loop's first step then refills
+  // right away.
+  if (issued == 3)
+    wait_vmcnt<2 * C::kDmaPerWave>();
+  else if (issued == 2)
+    wait_vmcnt<C::kDmaPerWave>();
+  else
+    wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  bf16x8 qf[8];
+  read_q<FP8>(qs, w, n, g, qf);
   Q8 q8;  // fp8 cache: q as hi/lo e4m3 pairs
   if constexpr (FP8) split_q8(qf, q8);
 
@@ -474,9 +497,12 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
 
   for (int t = 0; cons.valid(); ++t) {
     if (fresh) {
-      // Later pieces of the workgroup: a full drain for their Q (rare).
-      load_q<FP8>(a, cons.b, w, n, g, qf);
+      // Later pieces of the workgroup: a full drain for their q (rare). Every
+      // wave finished reading the previous q right after it landed.
+      issue_q(a, cons.b, qs, w, lane);
       wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      read_q<FP8>(qs, w, n, g, qf);
       if constexpr (FP8) split_q8(qf, q8);
       m_run = -INFINITY;  // the first block rescales acc by exp2(-inf) = 0
       piece_lo = cons.gpos - cons.seq_start;

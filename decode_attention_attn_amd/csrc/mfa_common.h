@@ -78,6 +78,8 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const MFA_LDS bf16x4* __restrict
 __device__ __forceinline__ i32x2 lds_read_tr8(const MFA_LDS i32x2* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MFA_LDS i32x2*)p);
 }
+// Plain 16-byte LDS read with the same alias-scope treatment.
+__device__ __forceinline__ bf16x8 lds_read_b128(const MFA_LDS bf16x8* __restrict__ p) { return *p; }
 
 // Cross-lane combine of the 4 lanes n, n+16, n+32, n+48 (one value per
 // 16-lane row) with the gfx950 row/half swaps: no LDS round trip.
