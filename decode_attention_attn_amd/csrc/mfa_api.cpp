@@ -56,6 +56,17 @@ bool act_dtype_ok(mfa_dtype dt) { return dt == MFA_F32 || dt == MFA_BF16; }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Compute units the projection plans are made for. Workspace sizes assume this
+// many (no device needed to size a workspace); a call plans for
+// min(device CUs, kPlanCus), and its split-K factor never exceeds the sized
+// one because it only grows with the CU count.
+constexpr int kPlanCus = 256;
+int plan_cus(int* status) {
+  if (status == nullptr) return kPlanCus;
+  const int c = current_cu_count(status);
+  return c < kPlanCus ? c : kPlanCus;
+}
+
 
 }  // namespace
 
@@ -78,18 +89,25 @@ const char* mfa_status_string(int status) {
 }
 
 // ------------------------------------------------------------------ q path
-static size_t qproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* plan_out) {
+// Workspace: partial sums (those of the down-projection, later reused by the
+// up-projection's), then the normalized latent c_hat. 0 on a device error.
+static size_t qproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* dn_out, mfa::GemmPlan* up_out, int* status) {
   const bool bf = dt == MFA_BF16;
-  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK);
-  if (plan_out) *plan_out = p;
-  const size_t part = bf ? mfa::gemm_partial_bytes(p) : (size_t)B * MFA_RANK * sizeof(float);
+  const int cus = plan_cus(status);
+  if (cus <= 0) return 0;
+  const mfa::GemmPlan dn = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK, cus);
+  const mfa::GemmPlan up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus);
+  if (dn_out) *dn_out = dn;
+  if (up_out) *up_out = up;
+  size_t part = bf ? mfa::gemm_partial_bytes(dn) : (size_t)B * MFA_RANK * sizeof(float);
+  if (bf && up.splits > 1 && mfa::gemm_partial_bytes(up) > part) part = mfa::gemm_partial_bytes(up);
   const size_t chat = (size_t)B * MFA_RANK * (bf ? 2 : 4);
   return align256(part) + align256(chat);
 }
 
 size_t mfa_qproj_workspace_size(int B, mfa_dtype dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(dt)) return 0;
-  return qproj_ws(B, dt, nullptr);
+  return qproj_ws(B, dt, nullptr, nullptr, nullptr);
 }
 
 int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq, void* q_out, void* ws,
@@ -100,34 +118,45 @@ int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, co
   if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(q_out) || !aligned16(ws) ||
       (gamma && !aligned_n(gamma, 4)))
     return MFA_ERR_ALIGNMENT;
-  mfa::GemmPlan plan;
-  const size_t need = qproj_ws(B, dt, &plan);
-  if (!ws || ws_bytes < need) return MFA_ERR_WORKSPACE;
+  // the documented size first (host only), then the device's own plan
+  if (!ws || ws_bytes < qproj_ws(B, dt, nullptr, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
+  mfa::GemmPlan plan, up;
+  int st = MFA_OK;
+  qproj_ws(B, dt, &plan, &up, &st);
+  if (st != MFA_OK) return st;
   const bool bf = dt == MFA_BF16;
   hipStream_t s = (hipStream_t)stream;
   float* part = (float*)ws;
-  void* chat = (char*)ws + align256(bf ? mfa::gemm_partial_bytes(plan) : (size_t)B * MFA_RANK * sizeof(float));
+  size_t part_bytes = bf ? mfa::gemm_partial_bytes(plan) : (size_t)B * MFA_RANK * sizeof(float);
+  if (bf && up.splits > 1 && mfa::gemm_partial_bytes(up) > part_bytes) part_bytes = mfa::gemm_partial_bytes(up);
+  void* chat = (char*)ws + align256(part_bytes);
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_dq, w_dq, part, mfa::GemmOut::Partial, s);
   if (e != hipSuccess) return hip_status(e);
   e = mfa::launch_rmsnorm_reduce(bf, part, bf ? plan.splits : 1, B, MFA_RANK, gamma, eps, chat, s);
   if (e != hipSuccess) return hip_status(e);
-  const mfa::GemmPlan up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM);
-  if (bf && up.splits != 1) return hip_status(hipErrorInvalidConfiguration);  // never: 128 column tiles
+  if (bf && up.splits > 1) {
+    // the down-projection's partials were consumed by the reduce above
+    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s));
+  }
   e = mfa::launch_gemm(bf, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s);
   return hip_status(e);
 }
 
 // ------------------------------------------------------------------ K/V append
-static size_t kv_ws(int B, mfa_dtype act_dt, mfa::GemmPlan* plan_out) {
+static size_t kv_ws(int B, mfa_dtype act_dt, mfa::GemmPlan* plan_out, int* status) {
   const bool bf = act_dt == MFA_BF16;
-  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM);
+  const int cus = plan_cus(status);
+  if (cus <= 0) return 0;
+  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM, cus);
   if (plan_out) *plan_out = p;
   return align256(bf ? mfa::gemm_partial_bytes(p) : (size_t)B * 2 * MFA_HEAD_DIM * sizeof(float));
 }
 
 size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(act_dt)) return 0;
-  return kv_ws(B, act_dt, nullptr);
+  return kv_ws(B, act_dt, nullptr, nullptr);
 }
 
 int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
@@ -139,9 +168,11 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
     return MFA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < kv_ws(B, act_dt, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
   mfa::GemmPlan plan;
-  const size_t need = kv_ws(B, act_dt, &plan);
-  if (!ws || ws_bytes < need) return MFA_ERR_WORKSPACE;
+  int st = MFA_OK;
+  kv_ws(B, act_dt, &plan, &st);
+  if (st != MFA_OK) return st;
   const bool bf = act_dt == MFA_BF16;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
@@ -209,16 +240,18 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
 }
 
 // ------------------------------------------------------------------ out-projection
-static size_t oproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* plan_out) {
+static size_t oproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* plan_out, int* status) {
   const bool bf = dt == MFA_BF16;
-  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN);
+  const int cus = plan_cus(status);
+  if (cus <= 0) return 0;
+  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN, cus);
   if (plan_out) *plan_out = p;
   return (bf && p.splits > 1) ? align256(mfa::gemm_partial_bytes(p)) : 0;
 }
 
 size_t mfa_oproj_workspace_size(int B, mfa_dtype dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(dt)) return 0;
-  return oproj_ws(B, dt, nullptr);
+  return oproj_ws(B, dt, nullptr, nullptr);
 }
 
 int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_bytes, int B, mfa_dtype dt,
@@ -226,9 +259,12 @@ int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_by
   if (!attn || !w_o || !y || B < 1 || B > MFA_MAX_BATCH) return MFA_ERR_INVALID_ARG;
   if (!act_dtype_ok(dt)) return MFA_ERR_UNSUPPORTED;
   if (!aligned16(attn) || !aligned16(w_o) || !aligned16(y) || !aligned16(ws)) return MFA_ERR_ALIGNMENT;
-  mfa::GemmPlan plan;
-  const size_t need = oproj_ws(B, dt, &plan);
+  const size_t need = oproj_ws(B, dt, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need)) return MFA_ERR_WORKSPACE;
+  mfa::GemmPlan plan;
+  int st = MFA_OK;
+  oproj_ws(B, dt, &plan, &st);
+  if (st != MFA_OK) return st;
   const bool bf = dt == MFA_BF16;
   hipStream_t s = (hipStream_t)stream;
   if (bf && plan.splits > 1) {

@@ -63,10 +63,12 @@ struct GemmPlan {
   int M, N, K, N0;
   int splits;   // S
   int mchunks;  // ceil(M / 128) (bf16 path)
+  int tile_n;   // output columns per workgroup: 128 or 256 (bf16 path)
 };
 
 // bf16: MFMA kernel; f32: VALU kernel (no split).
-GemmPlan plan_gemm(bool bf16, int M, int N, int K, int N0);
+// cus: compute units of the device (the split-K factor fills them once).
+GemmPlan plan_gemm(bool bf16, int M, int N, int K, int N0, int cus);
 size_t gemm_partial_bytes(const GemmPlan& p);
 hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
                        GemmOut mode, hipStream_t stream);

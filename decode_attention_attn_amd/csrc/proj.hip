@@ -21,14 +21,25 @@
 
 namespace mfa {
 
-constexpr int kGN = 128;    // output columns (weight rows) per workgroup
+constexpr int kGN = 128;    // output columns (weight rows) per workgroup (narrow tile)
 constexpr int kGM = 128;    // batch rows per workgroup
 constexpr int kGK = 64;     // K per stage
-constexpr int kGStages = 4;
-constexpr int kGTileBytes = 128 * kGK * 2;        // 16 KB: one operand tile
-constexpr int kGStageBytes = 2 * kGTileBytes;     // weights then activations
-constexpr int kGDmaPerWave = 2 * (kGTileBytes / 1024) / 4;  // 8
-constexpr int kGSteadyVm = (kGStages - 2) * kGDmaPerWave;   // 16
+
+// Tile shapes. Every wave owns 32 batch rows x 128 output columns. The wide
+// tile (8 waves, 256 columns) reads each activation chunk once per 256
+// weight rows instead of 128, which halves the activation share of the bytes
+// a workgroup streams; it is used for the wide products (the out-projection).
+template <int NW>
+struct GTile {
+  static constexpr int kN = NW;                      // output columns per workgroup
+  static constexpr int kWaves = NW / 32;             // 4 or 8
+  static constexpr int kStages = NW == 128 ? 4 : 3;  // LDS ring (64 KB or 48 KB stages)
+  static constexpr int kWBytes = NW * kGK * 2;       // weight tile
+  static constexpr int kXBytes = kGM * kGK * 2;      // activation tile (16 KB)
+  static constexpr int kStageBytes = kWBytes + kXBytes;
+  static constexpr int kDmaPerWave = (kStageBytes / 1024) / kWaves;  // 8 or 6
+  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;
+};
 
 struct GemmArgs {
   const bf16* X;
@@ -42,34 +53,52 @@ struct GemmArgs {
 // consecutive rows at one logical chunk for 32- and 64-bank LDS.
 __device__ __forceinline__ int gswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// One K chunk of the weight tile (T::kN rows) and the activation tile (128
+// rows) into a ring stage: 1 KB blocks of 8 rows x 128 B, dealt evenly to
+// the waves (weight blocks first).
+template <int NW>
 __device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, int kc, char* stage, int w, int lane) {
+  using T = GTile<NW>;
   const int r_in = lane >> 3;  // 8 rows of 128 B per 1 KB block
   const int pc = lane & 7;
   const int k0 = kc * kGK;
+  constexpr int kWBlocks = T::kWBytes / 1024;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int blk = 4 * w + jj;
-    const int r = 8 * blk + r_in;
-    const int c = pc ^ gswz(r);
-    const int n = n0 + r;
-    const bf16* wrow = n < a.N0 ? a.W0 + (long long)n * a.K : a.W1 + (long long)(n - a.N0) * a.K;
-    __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
-    int m = m0 + r;
-    m = m < a.M ? m : a.M - 1;
-    const bf16* xrow = a.X + (long long)m * a.K;
-    __builtin_amdgcn_global_load_lds((const void*)(xrow + k0 + c * 8),
-                                     (MFA_LDS void*)(stage + kGTileBytes + blk * 1024), 16, 0, 0);
+  for (int jj = 0; jj < T::kDmaPerWave; ++jj) {
+    const int blk = T::kDmaPerWave * w + jj;
+    if (blk < kWBlocks) {
+      const int r = 8 * blk + r_in;
+      const int c = pc ^ gswz(r);
+      const int n = n0 + r;
+      const bf16* wrow = n < a.N0 ? a.W0 + (long long)n * a.K : a.W1 + (long long)(n - a.N0) * a.K;
+      __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0,
+                                       0);
+    } else {
+      const int r = 8 * (blk - kWBlocks) + r_in;
+      const int c = pc ^ gswz(r);
+      int m = m0 + r;
+      m = m < a.M ? m : a.M - 1;
+      const bf16* xrow = a.X + (long long)m * a.K;
+      __builtin_amdgcn_global_load_lds((const void*)(xrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0,
+                                       0);
+    }
   }
 }
 
-template <GemmOut MODE>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+template <GemmOut MODE, int NW>
+__global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
+  using T = GTile<NW>;
+  constexpr int kGStages = T::kStages;
+  constexpr int kGStageBytes = T::kStageBytes;
+  constexpr int kGSteadyVm = T::kSteadyVm;
   __shared__ __attribute__((aligned(1024))) char ring[kGStages * kGStageBytes];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
+  const int w = wave & 3;            // batch rows 32w..32w+31 of the tile
+  const int wn = (wave >> 2) * 128;  // this wave's 128 output columns within the tile
   const int i16 = lane & 15;
   const int g = lane >> 4;
-  const int n0 = blockIdx.x * kGN;
+  const int n0 = blockIdx.x * T::kN;
   const int split = blockIdx.y;
   const int m0 = blockIdx.z * kGM;
   const int nch = a.K / kGK;
@@ -87,7 +116,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < kGStages - 1; ++s)
     if (issued < nloc) {
-      gemm_issue(a, n0, m0, c_begin + issued, ring + s * kGStageBytes, w, lane);
+      gemm_issue<NW>(a, n0, m0, c_begin + issued, ring + s * kGStageBytes, wave, lane);
       ++issued;
     }
 
@@ -98,11 +127,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (issued < nloc) {
-      gemm_issue(a, n0, m0, c_begin + issued, ring + ((t + kGStages - 1) % kGStages) * kGStageBytes, w, lane);
+      gemm_issue<NW>(a, n0, m0, c_begin + issued, ring + ((t + kGStages - 1) % kGStages) * kGStageBytes, wave, lane);
       ++issued;
     }
-    const char* ws = ring + (t % kGStages) * kGStageBytes;
-    const char* xs = ws + kGTileBytes;
+    const char* ws = ring + (t % kGStages) * kGStageBytes + wn * 128;
+    const char* xs = ring + (t % kGStages) * kGStageBytes + T::kWBytes;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = 4 * j + g;
@@ -132,7 +161,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     if (m >= a.M) continue;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const int n = n0 + 16 * nb + 4 * g;
+      const int n = n0 + wn + 16 * nb + 4 * g;
       if constexpr (MODE == GemmOut::Partial) {
         float* dst = (float*)a.Y + ((long long)split * a.M + m) * a.N + n;
         *(f32x4*)dst = acc[mi][nb];
@@ -178,21 +207,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const flo
 }
 
 // ------------------------------------------------------------------ epilogues
+// The epilogues are latency-bound (a few MB in total): every thread keeps
+// several independent 16-byte partial loads in flight instead of summing the
+// splits one dependent load at a time.
+
+// sum over s < S of the f32x4 at p + s * stride, 8 loads in flight.
+__device__ __forceinline__ f32x4 sum_splits(const float* p, long long stride, int S) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = s0 + k < S ? *(const f32x4*)(p + (s0 + k) * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v += t[k];
+  }
+  return v;
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* part, int S, int M, int N,
                                                              const float* gamma, float eps, OutT* out) {
-  // one block per row; N <= 4096 and N % 256 == 0
+  // one block per row; N <= 4096 and N % 1024 == 0: thread t owns columns
+  // 4t + 1024i .. +3
   const int m = blockIdx.x;
   const int t = threadIdx.x;
-  float c[16];
+  f32x4 c[4];
   float ss = 0.f;
-  const int per = N / 256;
-  for (int i = 0; i < per; ++i) {
-    const int col = t + 256 * i;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += part[((long long)s * M + m) * N + col];
-    c[i] = v;
-    ss = fmaf(v, v, ss);
+  const int per = N / 1024;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < per) {
+      c[i] = sum_splits(part + (long long)m * N + 4 * t + 1024 * i, (long long)M * N, S);
+      ss += c[i][0] * c[i][0] + c[i][1] * c[i][1] + c[i][2] * c[i][2] + c[i][3] * c[i][3];
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
@@ -201,11 +248,17 @@ __global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* part, 
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float r = rsqrtf(tot / (float)N + eps);
-  for (int i = 0; i < per; ++i) {
-    const int col = t + 256 * i;
-    float v = c[i] * r;
-    if (gamma != nullptr) v *= gamma[col];
-    out[(long long)m * N + col] = (OutT)v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < per) {
+      const int col = 4 * t + 1024 * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = c[i][e] * r;
+        if (gamma != nullptr) v *= gamma[col + e];
+        out[(long long)m * N + col + e] = (OutT)v;
+      }
+    }
   }
 }
 
@@ -214,8 +267,7 @@ __global__ __launch_bounds__(256) void sum_reduce_kernel(const float* part, int 
   const long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
   const long long total4 = (long long)M * N / 4;
   if (i4 >= total4) return;
-  f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) v += *(const f32x4*)(part + (long long)s * M * N + 4 * i4);
+  const f32x4 v = sum_splits(part + 4 * i4, (long long)M * N, S);
   OutT* dst = out + 4 * i4;
   dst[0] = (OutT)v[0];
   dst[1] = (OutT)v[1];
@@ -228,8 +280,7 @@ __global__ __launch_bounds__(128) void kv_scatter_kernel(const float* part, int 
                                                          const int64_t* seq_off, const int32_t* seq_len) {
   const int m = blockIdx.x;
   const int col = 4 * threadIdx.x;  // 0..508 of the [k | v] row
-  f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) v += *(const f32x4*)(part + ((long long)s * M + m) * 512 + col);
+  const f32x4 v = sum_splits(part + (long long)m * 512 + col, (long long)M * 512, S);
   const long long row = seq_off[m] + (long long)seq_len[m];
   OutT* dst = (col < 256 ? kc : vc) + row * 256 + (col & 255);
   dst[0] = (OutT)v[0];
@@ -239,18 +290,33 @@ __global__ __launch_bounds__(128) void kv_scatter_kernel(const float* part, int 
 }
 
 // ------------------------------------------------------------------ host side
-GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0) {
-  GemmPlan p{M, N, K, N0, 1, 1};
+GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) {
+  GemmPlan p{M, N, K, N0, 1, 1, kGN};
   if (!bf16_path) return p;
   p.mchunks = (M + kGM - 1) / kGM;
-  const int tiles = (N / kGN) * p.mchunks;
   const int nch = K / kGK;
-  // split K only until about half the CUs have a workgroup: partial sums cost
-  // 2 * S * M * N * 4 bytes of extra traffic.
-  int s = (128 + tiles - 1) / tiles;
-  if (s < 1) s = 1;
-  if (s > nch) s = nch;
-  p.splits = s;
+  // For each tile width, split K so that the workgroups fill the compute
+  // units once (one per CU; a second partial wave would only lengthen the
+  // tail), then pick the width with the smaller estimated time: each CU
+  // streams (tile_n + 128) * K / S * 2 bytes of weights and activations, and
+  // the partial sums add 2 * S * M * N * 4 bytes across the chip.
+  double best = 0.0;
+  for (int tn = 128; tn <= 256; tn *= 2) {
+    if (N % tn != 0) continue;
+    const int tiles = (N / tn) * p.mchunks;
+    int s = cus / tiles;
+    if (s < 1) s = 1;
+    if (s > nch) s = nch;
+    const int waves = (tiles * s + cus - 1) / cus;
+    const double per_cu = (double)(tn + kGM) * K / s * 2.0 * waves;  // bytes, ~30 GB/s per CU
+    const double partial = s > 1 ? 2.0 * s * M * (double)N * 4.0 : 0.0;  // bytes, ~5 TB/s chip-wide
+    const double t = per_cu / 30e9 + partial / 5e12;
+    if (best == 0.0 || t < best) {
+      best = t;
+      p.tile_n = tn;
+      p.splits = s;
+    }
+  }
   return p;
 }
 
@@ -263,11 +329,13 @@ hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const v
                        (const float*)W1, (float*)Y, p.M, p.N, p.K, p.N0);
   }
   GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits};
-  const dim3 grid(p.N / kGN, p.splits, p.mchunks);
-  if (mode == GemmOut::Partial)
-    return launch(gemm_bf16_kernel<GemmOut::Partial>, grid, dim3(256), stream, a);
-  else
-    return launch(gemm_bf16_kernel<GemmOut::Direct>, grid, dim3(256), stream, a);
+  const dim3 grid(p.N / p.tile_n, p.splits, p.mchunks);
+  if (p.tile_n == 256) {
+    if (mode == GemmOut::Partial) return launch(gemm_bf16_kernel<GemmOut::Partial, 256>, grid, dim3(512), stream, a);
+    return launch(gemm_bf16_kernel<GemmOut::Direct, 256>, grid, dim3(512), stream, a);
+  }
+  if (mode == GemmOut::Partial) return launch(gemm_bf16_kernel<GemmOut::Partial, 128>, grid, dim3(256), stream, a);
+  return launch(gemm_bf16_kernel<GemmOut::Direct, 128>, grid, dim3(256), stream, a);
 }
 
 hipError_t launch_rmsnorm_reduce(bool bf16_path, const float* part, int S, int M, int N, const float* gamma, float eps,
