@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 # Sources the attention kernels are built from: HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
 KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/attn.hip", "decode_attention_attn_amd/csrc/mfa_common.h",
-                  "decode_attention_attn_amd/csrc/mfa_internal.h"]
+                  "decode_attention_attn_amd/csrc/mfa_internal.h", "decode_attention_attn_amd/build.py"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 
