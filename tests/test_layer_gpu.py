@@ -86,6 +86,17 @@ def test_layer_bf16_small(G):
     _check_layer(inp, [0, 2, 4], "bf16", num_workgroups=G)
 
 
+@pytest.mark.parametrize("B", [1, 200])
+def test_layer_bf16_batch_edges(B):
+    # one sequence; and more sequences than one 128-row GEMM tile (a second,
+    # partly filled batch chunk in every projection)
+    print(f"[case] layer bf16 B={B} ctx=64", flush=True)
+    w = gen.scaled(gen.WORKLOADS["layer_bf16_8k"], batch=B, ctx=64)
+    inp = gen.make_layer(w)
+    ids = [0] if B == 1 else [0, 127, 128, 199]
+    _check_layer(inp, ids, "bf16")
+
+
 def test_layer_bf16_8k_full():
     print("[case] layer layer_bf16_8k (full size, sampled sequences)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_bf16_8k"])
