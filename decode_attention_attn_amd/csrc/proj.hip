@@ -211,47 +211,47 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const flo
 // several independent 16-byte partial loads in flight instead of summing the
 // splits one dependent load at a time.
 
-// sum over s < S of the f32x4 at p + s * stride, 8 loads in flight.
+// sum over s < S of the f32x4 at p + s * stride, 16 loads in flight.
 __device__ __forceinline__ f32x4 sum_splits(const float* p, long long stride, int S) {
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    f32x4 t[8];
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    f32x4 t[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) t[k] = s0 + k < S ? *(const f32x4*)(p + (s0 + k) * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 16; ++k) t[k] = s0 + k < S ? *(const f32x4*)(p + (s0 + k) * stride) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v += t[k];
+    for (int k = 0; k < 16; ++k) v += t[k];
   }
   return v;
 }
 
 template <typename OutT>
-__global__ __launch_bounds__(256) void rmsnorm_reduce_kernel(const float* part, int S, int M, int N,
+__global__ __launch_bounds__(512) void rmsnorm_reduce_kernel(const float* part, int S, int M, int N,
                                                              const float* gamma, float eps, OutT* out) {
-  // one block per row; N <= 4096 and N % 1024 == 0: thread t owns columns
-  // 4t + 1024i .. +3
+  // one block per row; N <= 8192 and N % 2048 == 0: thread t owns columns
+  // 4t + 2048i .. +3
   const int m = blockIdx.x;
   const int t = threadIdx.x;
   f32x4 c[4];
   float ss = 0.f;
-  const int per = N / 1024;
+  const int per = N / 2048;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < per) {
-      c[i] = sum_splits(part + (long long)m * N + 4 * t + 1024 * i, (long long)M * N, S);
+      c[i] = sum_splits(part + (long long)m * N + 4 * t + 2048 * i, (long long)M * N, S);
       ss += c[i][0] * c[i][0] + c[i][1] * c[i][1] + c[i][2] * c[i][2] + c[i][3] * c[i][3];
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  __shared__ float red[4];
+  __shared__ float red[8];
   if ((t & 63) == 0) red[t >> 6] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float tot = red[0] + red[1] + red[2] + red[3] + red[4] + red[5] + red[6] + red[7];
   const float r = rsqrtf(tot / (float)N + eps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < per) {
-      const int col = 4 * t + 1024 * i;
+      const int col = 4 * t + 2048 * i;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float v = c[i][e] * r;
@@ -305,8 +305,11 @@ GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) {
     if (N % tn != 0) continue;
     const int tiles = (N / tn) * p.mchunks;
     int s = cus / tiles;
+    // at least 4 K chunks per split: below that a workgroup is all start-up
+    // latency and the partial sums outgrow the weights
+    const int smax = nch / 4 > 0 ? nch / 4 : 1;
+    if (s > smax) s = smax;
     if (s < 1) s = 1;
-    if (s > nch) s = nch;
     const int waves = (tiles * s + cus - 1) / cus;
     const double per_cu = (double)(tn + kGM) * K / s * 2.0 * waves;  // bytes, ~30 GB/s per CU
     const double partial = s > 1 ? 2.0 * s * M * (double)N * 4.0 : 0.0;  // bytes, ~5 TB/s chip-wide
@@ -341,10 +344,10 @@ hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const v
 hipError_t launch_rmsnorm_reduce(bool bf16_path, const float* part, int S, int M, int N, const float* gamma, float eps,
                                  void* out, hipStream_t stream) {
   if (bf16_path)
-    return launch(rmsnorm_reduce_kernel<bf16>, dim3(M), dim3(256), stream, part, S, M, N, gamma, eps,
+    return launch(rmsnorm_reduce_kernel<bf16>, dim3(M), dim3(512), stream, part, S, M, N, gamma, eps,
                        (bf16*)out);
   else
-    return launch(rmsnorm_reduce_kernel<float>, dim3(M), dim3(256), stream, part, S, M, N, gamma, eps,
+    return launch(rmsnorm_reduce_kernel<float>, dim3(M), dim3(512), stream, part, S, M, N, gamma, eps,
                        (float*)out);
 }
 
