@@ -353,6 +353,10 @@ struct VReader {
       sw = swz_v8(r);
     }
   }
+  // fp8: the 8 raw bytes (widened with widen8)
+  __device__ __forceinline__ i32x2 read8(const char* vs, int db) const {
+    return lds_read_tr8((const MFA_LDS i32x2*)(vs + base + ((db ^ sw) << 4)));
+  }
   __device__ __forceinline__ bf16x8 read(const char* vs, int db) const {
     if constexpr (!FP8) {
       const int lc = 2 * db + lc_lo;
@@ -369,50 +373,19 @@ struct VReader {
   }
 };
 
-// One 32-row block: scores, online softmax update, PV accumulate.
-template <bool FP8>
-__device__ __forceinline__ void attend_block(const char* ks, const char* vs, int nvalid, int n, int g,
-                                             const VReader<FP8>& vr, const bf16x8 (&qf)[8], const Q8& q8,
-                                             float score_mul, float& m_run, float& l_run, f32x4 (&acc)[16]) {
-  // K fragments first, then the score MFMAs interleaved with the V reads (V
-  // does not depend on the scores), so that LDS latency overlaps matrix work.
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 vf[16];
-  if constexpr (!FP8) {
-    bf16x8 kf0[8], kf1[8];
-    read_k<FP8>(ks, n, g, kf0, 0);
-    read_k<FP8>(ks, n, g, kf1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[j], qf[j], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[j], qf[j], s1, 0, 0, 0);
-      vf[2 * j] = vr.read(vs, 2 * j);
-      vf[2 * j + 1] = vr.read(vs, 2 * j + 1);
-    }
-  } else {
-    i32x8 k00 = read_k8(ks, n, g, 0, 0), k01 = read_k8(ks, n, g, 0, 1);
-    i32x8 k10 = read_k8(ks, n, g, 1, 0), k11 = read_k8(ks, n, g, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 l0 = s0, l1 = s0;  // lo parts
-    s0 = mfma_fp8_k128(k00, q8.hi[0], s0);
-    s1 = mfma_fp8_k128(k10, q8.hi[0], s1);
-    l0 = mfma_fp8_k128(k00, q8.lo[0], l0);
-    l1 = mfma_fp8_k128(k10, q8.lo[0], l1);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) vf[db] = vr.read(vs, db);
-    s0 = mfma_fp8_k128(k01, q8.hi[1], s0);
-    s1 = mfma_fp8_k128(k11, q8.hi[1], s1);
-    l0 = mfma_fp8_k128(k01, q8.lo[1], l0);
-    l1 = mfma_fp8_k128(k11, q8.lo[1], l1);
-#pragma unroll
-    for (int db = 8; db < 16; ++db) vf[db] = vr.read(vs, db);
-    s0 += l0 * 0.0625f;
-    s1 += l1 * 0.0625f;
-    score_mul *= q8.mul;
-  }
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ bf16x8 widen8(const i32x2& raw) {
+  bf16x8 v;
+  fp8x4_to_bf16((unsigned)raw[0], v, 0);
+  fp8x4_to_bf16((unsigned)raw[1], v, 4);
+  return v;
+}
 
+// Online-softmax update and value product of one 32-row block whose scores
+// (before score_mul) are s0 (rows 4g+i) and s1 (rows 16+4g+i) of head n; vf
+// holds the block's V^T operands. Rows at or past nvalid are masked (a block
+// with none left changes nothing once m_run is finite).
+__device__ __forceinline__ void softmax_pv(const f32x4& s0, const f32x4& s1, int nvalid, int g, float score_mul,
+                                           const bf16x8 (&vf)[16], float& m_run, float& l_run, f32x4 (&acc)[16]) {
   float sc[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -442,6 +415,78 @@ __device__ __forceinline__ void attend_block(const char* ks, const char* vs, int
   const bf16x8 pf = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3], (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
 #pragma unroll
   for (int db = 0; db < 16; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, acc[db], 0, 0, 0);
+}
+
+// One 32-row bf16 tile: scores, online softmax update, PV accumulate. The K
+// fragments are read first, then the score MFMAs are interleaved with the V
+// reads (V does not depend on the scores), so that LDS latency overlaps
+// matrix work.
+__device__ __forceinline__ void attend_tile_bf16(const char* ks, const char* vs, int nvalid, int n, int g,
+                                                 const VReader<false>& vr, const bf16x8 (&qf)[8], float score_mul,
+                                                 float& m_run, float& l_run, f32x4 (&acc)[16]) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 vf[16];
+  bf16x8 kf0[8], kf1[8];
+  read_k<false>(ks, n, g, kf0, 0);
+  read_k<false>(ks, n, g, kf1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[j], qf[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[j], qf[j], s1, 0, 0, 0);
+    vf[2 * j] = vr.read(vs, 2 * j);
+    vf[2 * j + 1] = vr.read(vs, 2 * j + 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  softmax_pv(s0, s1, nvalid, g, score_mul, vf, m_run, l_run, acc);
+}
+
+// Scores of the fp8 32-row block at ks, before score_mul: rows 4g+i (s0) and
+// 16+4g+i (s1) of head n, as hi + lo / 16 products.
+__device__ __forceinline__ void scores_fp8(const char* ks, int n, int g, const Q8& q8, f32x4& s0, f32x4& s1) {
+  const i32x8 k00 = read_k8(ks, n, g, 0, 0), k01 = read_k8(ks, n, g, 0, 1);
+  const i32x8 k10 = read_k8(ks, n, g, 1, 0), k11 = read_k8(ks, n, g, 1, 1);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 l0 = mfma_fp8_k128(k00, q8.lo[0], z);
+  f32x4 l1 = mfma_fp8_k128(k10, q8.lo[0], z);
+  s0 = mfma_fp8_k128(k00, q8.hi[0], z);
+  s1 = mfma_fp8_k128(k10, q8.hi[0], z);
+  l0 = mfma_fp8_k128(k01, q8.lo[1], l0);
+  l1 = mfma_fp8_k128(k11, q8.lo[1], l1);
+  s0 = mfma_fp8_k128(k01, q8.hi[1], s0);
+  s1 = mfma_fp8_k128(k11, q8.hi[1], s1);
+  s0 += l0 * 0.0625f;
+  s1 += l1 * 0.0625f;
+}
+
+// One 64-row fp8 tile as two 32-row blocks, ordered so that matrix and vector
+// work of the two blocks overlap within the wave: both blocks' score products
+// are issued before the first block's softmax (which then runs on the vector
+// unit while the second block's products execute), and the second block's
+// softmax and V widening follow the issue of the first block's value product.
+__device__ __forceinline__ void attend_tile_fp8(const char* ks, const char* vs, int nvalid, int n, int g,
+                                                const VReader<true>& vr, const Q8& q8, float score_mul, float& m_run,
+                                                float& l_run, f32x4 (&acc)[16]) {
+  constexpr int kBlk = 32 * 256;  // bytes of a 32-row block of K or V
+  score_mul *= q8.mul;
+  f32x4 a0, a1, b0, b1;
+  i32x2 v8[16];
+  bf16x8 vf[16];
+  scores_fp8(ks, n, g, q8, a0, a1);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) v8[db] = vr.read8(vs, db);
+  // rows past nvalid are masked, so the second block needs no branch
+  scores_fp8(ks + kBlk, n, g, q8, b0, b1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) vf[db] = widen8(v8[db]);
+  softmax_pv(a0, a1, nvalid, g, score_mul, vf, m_run, l_run, acc);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) v8[db] = vr.read8(vs + kBlk, db);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) vf[db] = widen8(v8[db]);
+  softmax_pv(b0, b1, nvalid - 32, g, score_mul, vf, m_run, l_run, acc);
 }
 
 template <bool FP8>
@@ -523,12 +568,10 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     long long lo, hi;
     cons.tile(lo, hi);
     const int nvalid = (int)(hi - lo);
-    attend_block<FP8>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, q8, a.score_mul, m_run, l_run, acc);
-    if constexpr (FP8) {
-      if (nvalid > 32)
-        attend_block<FP8>(stage + 32 * C::kRowBytes, stage + C::kHalfBytes + 32 * C::kRowBytes, nvalid - 32, n, g,
-                          vr, qf, q8, a.score_mul, m_run, l_run, acc);
-    }
+    if constexpr (FP8)
+      attend_tile_fp8(stage, stage + C::kHalfBytes, nvalid, n, g, vr, q8, a.score_mul, m_run, l_run, acc);
+    else
+      attend_tile_bf16(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
 
     const long long pe = cons.part_end() - cons.seq_start;
     if (hi == pe) {
@@ -703,17 +746,21 @@ __global__ __launch_bounds__(256) void attn_combine_f32_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
   const int d0 = 4 * lane;
+  // the length and the piece record are loaded together (one round trip);
+  // the record is written by the attention kernel for every non-empty
+  // sequence and is not looked at for an empty one
   const long long L = load_scalar(a.seq_len, b);
+  const i32x2 rec = load_scalar((const i32x2*)a.meta, b);
   float* orow = (float*)a.out + ((long long)b * kHeads + h) * kHeadDim + d0;
-  if (L == 0) {
+  // (np >= 0 always: the test only keeps the record load ahead of the branch)
+  if ((L == 0) | (rec[1] < 0)) {
     *(f32x4*)orow = f32x4{0.f, 0.f, 0.f, 0.f};
     if (a.lse != nullptr && lane == 0) a.lse[(long long)b * kHeads + h] = -INFINITY;
     return;
   }
-  // written by the attention kernel for every non-empty sequence
-  const int np = load_scalar(a.meta, 2LL * b + 1);
+  const int np = rec[1];
   if (np == 0) return;
-  const long long slot0 = load_scalar(a.meta, 2LL * b);
+  const long long slot0 = rec[0];
   const float* lrow = a.part_lse + slot0 * kHeads + h;
   const float* prow = (const float*)a.part_o + (slot0 * kHeads + h) * kHeadDim + d0;
   constexpr int kBatch = 8;
@@ -757,19 +804,22 @@ __global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
   const int lane = c & 63, dp = (c >> 6) & 7, w = c >> 9;
   const int n = lane & 15, g = lane >> 4;
   const int h = 16 * w + n;
+  // length and piece record in one round trip (the record of an empty
+  // sequence is never written and not looked at)
   const long long L = load_scalar(a.seq_len, b);
+  const i32x2 rec = load_scalar((const i32x2*)a.meta, b);
   bf16* orow = (bf16*)a.out + ((long long)b * kHeads + h) * kHeadDim + 32 * dp + 4 * g;
   const bool lse_owner = a.lse != nullptr && dp == 0 && g == 0;
-  if (L == 0) {
+  // (np >= 0 always: the test only keeps the record load ahead of the branch)
+  if ((L == 0) | (rec[1] < 0)) {
     *(bf16x4*)orow = bf16x4{};
     *(bf16x4*)(orow + 16) = bf16x4{};
     if (lse_owner) a.lse[(long long)b * kHeads + h] = -INFINITY;
     return;
   }
-  // written by the attention kernel for every non-empty sequence
-  const int np = load_scalar(a.meta, 2LL * b + 1);
+  const int np = rec[1];
   if (np == 0) return;
-  const long long slot0 = load_scalar(a.meta, 2LL * b);
+  const long long slot0 = rec[0];
   const float* lrow = a.part_lse + slot0 * kHeads + h;
   const bf16x8* prow = (const bf16x8*)a.part_o + slot0 * (kHeads * kHeadDim / 8) + c;
   constexpr int kBatch = 8;

@@ -126,10 +126,11 @@ def test_workspace_reuse_across_batch_sizes():
         assert np.array_equal(outs[i][0], outs[i + 2][0]) and np.array_equal(outs[i][1], outs[i + 2][1])
 
 
-def test_splits_agree_and_repeat_bitwise():
+@pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
+def test_splits_agree_and_repeat_bitwise(kind):
     r = _runner()
-    print("[case] split agreement / determinism", flush=True)
-    inp = _make("bf16", lengths=[3000, 17, 1500, 4096])
+    print(f"[case] split agreement / determinism {kind}", flush=True)
+    inp = _make(kind, lengths=[3000, 17, 1500, 4096])
     outs = {}
     for G in (1, 5, 37, 0):
         o, _, _ = r.decode_attn(inp, num_workgroups=G)
