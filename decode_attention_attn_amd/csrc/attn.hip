@@ -470,22 +470,22 @@ __device__ __forceinline__ void attend_tile_fp8(const char* ks, const char* vs, 
   constexpr int kBlk = 32 * 256;  // bytes of a 32-row block of K or V
   score_mul *= q8.mul;
   f32x4 a0, a1, b0, b1;
-  i32x2 v8[16];
+  i32x2 v8[16], w8[16];
   bf16x8 vf[16];
   scores_fp8(ks, n, g, q8, a0, a1);
 #pragma unroll
   for (int db = 0; db < 16; ++db) v8[db] = vr.read8(vs, db);
   // rows past nvalid are masked, so the second block needs no branch
   scores_fp8(ks + kBlk, n, g, q8, b0, b1);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) w8[db] = vr.read8(vs + kBlk, db);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < 16; ++db) vf[db] = widen8(v8[db]);
   softmax_pv(a0, a1, nvalid, g, score_mul, vf, m_run, l_run, acc);
-#pragma unroll
-  for (int db = 0; db < 16; ++db) v8[db] = vr.read8(vs + kBlk, db);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int db = 0; db < 16; ++db) vf[db] = widen8(v8[db]);
+  for (int db = 0; db < 16; ++db) vf[db] = widen8(w8[db]);
   softmax_pv(b0, b1, nvalid - 32, g, score_mul, vf, m_run, l_run, acc);
 }
 
