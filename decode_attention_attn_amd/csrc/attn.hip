@@ -318,11 +318,10 @@ __device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// K operand (A of S^T = K Q^T) for rows 16pb..16pb+15 of the 32-row block at
-// ks: kf[j] holds the 8 channels of k-slot group g at step j for row 16pb + n.
-template <bool FP8>
+// bf16 K operand (A of S^T = K Q^T) for rows 16pb..16pb+15 of the 32-row
+// block at ks: kf[j] holds the 8 channels of k-slot group g at step j for row
+// 16pb + n. (The fp8 score product reads K with read_k8.)
 __device__ __forceinline__ void read_k(const char* ks, int n, int g, bf16x8 (&kf)[8], int pb) {
-  static_assert(!FP8, "the fp8 score product reads K with read_k8");
 #pragma unroll
   for (int j = 0; j < 8; ++j) kf[j] = *(const MFA_LDS bf16x8*)(ks + (16 * pb + n) * 512 + (((4 * j + g) ^ n) << 4));
 }
@@ -353,23 +352,18 @@ struct VReader {
       sw = swz_v8(r);
     }
   }
-  // fp8: the 8 raw bytes (widened with widen8)
+  // fp8: the 8 raw bytes of the fragment (widened with widen8)
   __device__ __forceinline__ i32x2 read8(const char* vs, int db) const {
+    static_assert(FP8, "bf16 fragments are read with read");
     return lds_read_tr8((const MFA_LDS i32x2*)(vs + base + ((db ^ sw) << 4)));
   }
+  // bf16: the fragment
   __device__ __forceinline__ bf16x8 read(const char* vs, int db) const {
-    if constexpr (!FP8) {
-      const int lc = 2 * db + lc_lo;
-      const bf16x4 lo = lds_read_tr16((const MFA_LDS bf16x4*)(vs + base0 + ((lc ^ sw0) << 4)));
-      const bf16x4 hi = lds_read_tr16((const MFA_LDS bf16x4*)(vs + base1 + ((lc ^ sw1) << 4)));
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      const i32x2 raw = lds_read_tr8((const MFA_LDS i32x2*)(vs + base + ((db ^ sw) << 4)));
-      bf16x8 v;
-      fp8x4_to_bf16((unsigned)raw[0], v, 0);
-      fp8x4_to_bf16((unsigned)raw[1], v, 4);
-      return v;
-    }
+    static_assert(!FP8, "fp8 fragments are read with read8");
+    const int lc = 2 * db + lc_lo;
+    const bf16x4 lo = lds_read_tr16((const MFA_LDS bf16x4*)(vs + base0 + ((lc ^ sw0) << 4)));
+    const bf16x4 hi = lds_read_tr16((const MFA_LDS bf16x4*)(vs + base1 + ((lc ^ sw1) << 4)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 };
 
@@ -427,8 +421,8 @@ __device__ __forceinline__ void attend_tile_bf16(const char* ks, const char* vs,
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   bf16x8 vf[16];
   bf16x8 kf0[8], kf1[8];
-  read_k<false>(ks, n, g, kf0, 0);
-  read_k<false>(ks, n, g, kf1, 1);
+  read_k(ks, n, g, kf0, 0);
+  read_k(ks, n, g, kf1, 1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
