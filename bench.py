@@ -197,7 +197,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn_bf16_4k",
-                    choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "layer_bf16_8k", "tiny_fp32"])
+                    choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "layer_bf16_8k", "layer_bf16_fp8kv_8k",
+                             "tiny_fp32"])
     ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

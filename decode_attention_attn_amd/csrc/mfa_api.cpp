@@ -181,6 +181,34 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
   return hip_status(e);
 }
 
+int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
+                      const int64_t* seq_off, const int32_t* seq_len, float k_scale, float v_scale, void* ws,
+                      size_t ws_bytes, int B, mfa_dtype act_dt, void* stream) {
+  if (!x || !w_k || !w_v || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 || B > MFA_MAX_BATCH)
+    return MFA_ERR_INVALID_ARG;
+  // the stored byte is e4m3(x * (1 / scale)): the reciprocal must be finite and non-zero
+  const float inv_k = 1.f / k_scale, inv_v = 1.f / v_scale;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale) || !isfinite(inv_k) ||
+      !isfinite(inv_v) || !(inv_k > 0.f) || !(inv_v > 0.f))
+    return MFA_ERR_INVALID_ARG;
+  if (!act_dtype_ok(act_dt)) return MFA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
+    return MFA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < kv_ws(B, act_dt, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
+  mfa::GemmPlan plan;
+  int st = MFA_OK;
+  kv_ws(B, act_dt, &plan, &st);
+  if (st != MFA_OK) return st;
+  const bool bf = act_dt == MFA_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = mfa::launch_kv_scatter_fp8((const float*)ws, bf ? plan.splits : 1, B, k_cache, v_cache, seq_off, seq_len,
+                                 inv_k, inv_v, s);
+  return hip_status(e);
+}
+
 // ------------------------------------------------------------------ attention
 size_t mfa_decode_attn_workspace_size(int B, int num_workgroups) {
   if (B < 1 || B > MFA_MAX_BATCH || num_workgroups < 0 || num_workgroups > 65536) return 0;

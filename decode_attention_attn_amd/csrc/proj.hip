@@ -289,6 +289,28 @@ __global__ __launch_bounds__(128) void kv_scatter_kernel(const float* part, int 
   dst[3] = (OutT)v[3];
 }
 
+// The same rows into an e4m3 cache: stored byte = e4m3(x / scale) with round to
+// nearest even, the quotient taken as x * inv (inv = 1 / scale rounded to fp32
+// on the host) and clamped to the largest finite magnitude, 448 (NaN stays NaN).
+__global__ __launch_bounds__(128) void kv_scatter_fp8_kernel(const float* part, int S, int M, unsigned char* kc,
+                                                             unsigned char* vc, const int64_t* seq_off,
+                                                             const int32_t* seq_len, float inv_k, float inv_v) {
+  const int m = blockIdx.x;
+  const int col = 4 * threadIdx.x;  // 0..508 of the [k | v] row
+  const f32x4 v = sum_splits(part + (long long)m * 512 + col, (long long)M * 512, S);
+  const float inv = col < 256 ? inv_k : inv_v;
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = v[i] * inv;
+    x[i] = t > 448.f ? 448.f : (t < -448.f ? -448.f : t);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);  // bytes 0, 1
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);       // bytes 2, 3
+  const long long row = seq_off[m] + (long long)seq_len[m];
+  *(int*)((col < 256 ? kc : vc) + row * 256 + (col & 255)) = w;
+}
+
 // ------------------------------------------------------------------ host side
 GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) {
   GemmPlan p{M, N, K, N0, 1, 1, kGN};
@@ -368,6 +390,13 @@ hipError_t launch_kv_scatter(bool bf16_path, const float* part, int S, int M, vo
   else
     return launch(kv_scatter_kernel<float>, dim3(M), dim3(128), stream, part, S, M, (float*)k_cache,
                        (float*)v_cache, seq_off, seq_len);
+}
+
+hipError_t launch_kv_scatter_fp8(const float* part, int S, int M, void* k_cache, void* v_cache,
+                                 const int64_t* seq_off, const int32_t* seq_len, float inv_k, float inv_v,
+                                 hipStream_t stream) {
+  return launch(kv_scatter_fp8_kernel, dim3(M), dim3(128), stream, part, S, M, (unsigned char*)k_cache,
+                (unsigned char*)v_cache, seq_off, seq_len, inv_k, inv_v);
 }
 
 }  // namespace mfa

@@ -177,6 +177,10 @@ WORKLOADS: Dict[str, Workload] = {
     "layer_bf16_8k": Workload(
         "layer_bf16_8k", "layer", 128, 8192, BF16, BF16,
         description="bf16 decode layer, batch 128, 8192 cached rows + 1 appended (8193 attended)"),
+    "layer_bf16_fp8kv_8k": Workload(
+        "layer_bf16_fp8kv_8k", "layer", 128, 8192, BF16, FP8,
+        description="bf16 decode layer over an e4m3fn K/V cache (per-tensor scales, new rows quantized on "
+                    "append), batch 128, 8192 cached rows + 1 appended"),
 }
 
 
@@ -218,6 +222,7 @@ def make_attn(w: Workload, lengths: Optional[np.ndarray] = None) -> dict:
 
 
 CANARY = 1234.0  # value left in cache rows that the step must not read before writing
+CANARY_E4M3 = 0x7F  # the same for an e4m3 cache: the NaN code
 
 
 def make_layer(w: Workload) -> dict:
@@ -233,13 +238,23 @@ def make_layer(w: Workload) -> dict:
     w_k = store(weight(w.seed, ID_WK, HEAD_DIM, HIDDEN), w.act)
     w_v = store(weight(w.seed, ID_WV, HEAD_DIM, HIDDEN), w.act)
     w_o = store(weight(w.seed, ID_WO, HIDDEN, QDIM), w.act)
-    caches = []
+    caches, scales = [], []
     for tid in (ID_K, ID_V):
         draws = normal(w.seed, tid, (B * ctx, HEAD_DIM)).reshape(B, ctx, HEAD_DIM)
-        full = np.full((B, ctx + 1, HEAD_DIM), CANARY, dtype=np.float32)
-        full[:, :ctx, :] = draws
-        caches.append(store(full.reshape(total_rows, HEAD_DIM), w.kv))
+        if w.kv == FP8:
+            # per-tensor scale from the cached draws; the free row holds the
+            # NaN code, so reading it before the append would poison the output
+            codes, sc = quantize_e4m3fn(draws)
+            full = np.full((B, ctx + 1, HEAD_DIM), CANARY_E4M3, dtype=np.uint8)
+            full[:, :ctx, :] = codes
+            caches.append(full.reshape(total_rows, HEAD_DIM))
+            scales.append(sc)
+        else:
+            full = np.full((B, ctx + 1, HEAD_DIM), CANARY, dtype=np.float32)
+            full[:, :ctx, :] = draws
+            caches.append(store(full.reshape(total_rows, HEAD_DIM), w.kv))
+            scales.append(None)
     return dict(workload=w, x=x, w_dq=w_dq, w_uq=w_uq, w_k=w_k, w_v=w_v, w_o=w_o,
-                k_cache=caches[0], v_cache=caches[1], seq_off=off,
+                k_cache=caches[0], v_cache=caches[1], k_scale=scales[0], v_scale=scales[1], seq_off=off,
                 seq_len=np.full(B, ctx, dtype=np.int32), capacity=cap,
                 kind_act=w.act, kind_kv=w.kv, eps=1e-6)

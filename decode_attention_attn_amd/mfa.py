@@ -55,6 +55,8 @@ _lib.mfa_kv_append_workspace_size.restype = _Z
 _lib.mfa_kv_append_workspace_size.argtypes = [_I, _I]
 _lib.mfa_kv_append.restype = _I
 _lib.mfa_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]
+_lib.mfa_kv_append_fp8.restype = _I
+_lib.mfa_kv_append_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _Z, _I, _I, _P]
 _lib.mfa_decode_attn_workspace_size.restype = _Z
 _lib.mfa_decode_attn_workspace_size.argtypes = [_I, _I]
 _lib.mfa_decode_attn.restype = _I
@@ -67,7 +69,7 @@ _lib.mfa_oproj.argtypes = [_P, _P, _P, _P, _Z, _I, _I, _P]
 EXPORTED = [
     "mfa_version", "mfa_status_string", "mfa_last_hip_error",
     "mfa_qproj_workspace_size", "mfa_qproj",
-    "mfa_kv_append_workspace_size", "mfa_kv_append",
+    "mfa_kv_append_workspace_size", "mfa_kv_append", "mfa_kv_append_fp8",
     "mfa_decode_attn_workspace_size", "mfa_decode_attn",
     "mfa_oproj_workspace_size", "mfa_oproj",
 ]
@@ -137,6 +139,13 @@ def mfa_kv_append_workspace_size(B: int, act_dt: int) -> int:
 def mfa_kv_append(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, ws, B, act_dt, cache_dt, stream=None) -> int:
     return _lib.mfa_kv_append(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off),
                               _ptr(seq_len), _ptr(ws), _nbytes(ws), B, act_dt, cache_dt, _stream(stream))
+
+
+def mfa_kv_append_fp8(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, k_scale, v_scale, ws, B, act_dt,
+                      stream=None) -> int:
+    return _lib.mfa_kv_append_fp8(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off),
+                                  _ptr(seq_len), float(k_scale), float(v_scale), _ptr(ws), _nbytes(ws), B, act_dt,
+                                  _stream(stream))
 
 
 def mfa_decode_attn_workspace_size(B: int, num_workgroups: int = 0) -> int:

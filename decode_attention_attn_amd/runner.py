@@ -105,7 +105,9 @@ def upload_layer(inp: dict, device="cuda") -> dict:
     d = {n: to_device(inp[n], ka, device) for n in ("x", "w_dq", "w_uq", "w_k", "w_v", "w_o")}
     d.update(k=to_device(inp["k_cache"], kk, device), v=to_device(inp["v_cache"], kk, device),
              off=to_device(inp["seq_off"], "i64", device), len=to_device(inp["seq_len"], "i32", device),
-             kind_act=ka, kind_kv=kk, B=len(inp["seq_len"]), eps=float(inp.get("eps", 1e-6)))
+             kind_act=ka, kind_kv=kk, B=len(inp["seq_len"]), eps=float(inp.get("eps", 1e-6)),
+             k_scale=float(inp["k_scale"]) if inp.get("k_scale") is not None else 1.0,
+             v_scale=float(inp["v_scale"]) if inp.get("v_scale") is not None else 1.0)
     return d
 
 
@@ -136,12 +138,17 @@ class LayerCall:
         B = d["B"]
         mfa.check(mfa.mfa_qproj(d["x"], d["w_dq"], None, d["eps"], d["w_uq"], self.q, self.ws_q, B, dt, s),
                   "mfa_qproj")
-        mfa.check(mfa.mfa_kv_append(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"], self.ws_kv, B,
-                                    dt, _DT[d["kind_kv"]], s), "mfa_kv_append")
+        if d["kind_kv"] == FP8:
+            mfa.check(mfa.mfa_kv_append_fp8(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"],
+                                            d["k_scale"], d["v_scale"], self.ws_kv, B, dt, s), "mfa_kv_append_fp8")
+        else:
+            mfa.check(mfa.mfa_kv_append(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"], self.ws_kv,
+                                        B, dt, _DT[d["kind_kv"]], s), "mfa_kv_append")
         # the appended row is attended: length + 1 (the caller owns seq_len)
         torch.add(d["len"], 1, out=self.len_after)
-        mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE, 1.0, 1.0,
-                                      self.o, self.lse, self.ws_a, B, self.G, dt, _DT[d["kind_kv"]], s),
+        mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
+                                      d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
+                                      _DT[d["kind_kv"]], s),
                   "mfa_decode_attn")
         mfa.check(mfa.mfa_oproj(self.o, d["w_o"], self.y, self.ws_o, B, dt, s), "mfa_oproj")
         return self

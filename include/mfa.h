@@ -99,6 +99,23 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
                   const int64_t* seq_off, const int32_t* seq_len, void* ws, size_t ws_bytes, int B,
                   mfa_dtype act_dt, mfa_dtype cache_dt, void* stream);
 
+/* ------------------------------------------------------------------ K/V append, e4m3 cache
+ * As mfa_kv_append, but the rows are stored quantized into e4m3 caches (the
+ * model runs in FP8, attention included: Step-3 summary, "Key claims"), the
+ * cache format mfa_decode_attn reads with kv_dt = MFA_FP8_E4M3 and the same
+ * per-tensor scales. Byte j of the new row is e4m3(x_j / scale) (OCP E4M3,
+ * "fn" variant: no infinity), rounded to nearest with ties to even, the
+ * quotient computed in fp32 as x_j * (1 / scale) with the reciprocal rounded
+ * to fp32, and clamped to +-448, the largest finite magnitude. k_scale and
+ * v_scale are host values, finite, > 0, with finite reciprocals (else
+ * MFA_ERR_INVALID_ARG). act_dt = MFA_F32 or MFA_BF16. Caches [rows, 256]
+ * bytes, 16-byte aligned. ws: at least mfa_kv_append_workspace_size(B, act_dt)
+ * bytes. Same device-side precondition as mfa_kv_append.
+ */
+int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
+                      const int64_t* seq_off, const int32_t* seq_len, float k_scale, float v_scale,
+                      void* ws, size_t ws_bytes, int B, mfa_dtype act_dt, void* stream);
+
 /* ------------------------------------------------------------------ attention
  * Shared-KV decode attention (Step-3 summary, "Key claims"/"Method": 64 query
  * heads attend over one shared K and one shared V head of width 256). For each

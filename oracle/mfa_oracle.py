@@ -28,7 +28,11 @@ Readings where the pages are silent (each one is a choice this library makes):
   * the single new query attends to every cached row of its sequence, the row
     appended in this step included; no mask;
   * log-sum-exp uses the natural log; a sequence with no rows gives output 0
-    and lse = -inf.
+    and lse = -inf;
+  * an fp8 cache is OCP E4M3 ("fn") bytes with one float32 scale per tensor
+    (the model runs in FP8, attention included: Step-3 summary, "Key
+    claims"); a new row is stored as e4m3(x / scale), rounded to nearest with
+    ties to even and saturated at +-448.
 
 Parity pins: every function here is checked against closed forms, hand-worked
 fixtures, invariants and a pure-Python brute force in tests/test_oracle_cpu.py.
@@ -75,6 +79,44 @@ def e4m3fn_table() -> np.ndarray:
 
 
 _E4M3 = e4m3fn_table()
+
+
+E4M3_MAX = 448.0
+
+
+def encode_e4m3fn(y) -> np.ndarray:
+    """float64 values -> OCP FP8 E4M3 ("fn") bytes, round to nearest, ties to even.
+
+    Written from the format definition above: in the normal range
+    (|y| >= 2^-6) write |y| = 2^e * f with f in [1, 2); the neighbours are
+    2^e * (1 + k/8), so k = round_half_even(8 (f - 1)), k = 8 carrying into
+    the next binade. Below 2^-6 the step is 2^-9: k = round_half_even(|y| 2^9)
+    is the subnormal code itself (k = 8 lands on 2^-6, code 0x08). Magnitudes
+    above 448, the largest finite value, saturate to 448 (the quantizer clamps
+    before rounding); NaN gives 0x7F; the sign bit follows signbit(y).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    codes = np.zeros(y.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    codes[sub] = np.rint(a[sub] * 512.0).astype(np.int64)
+    nrm = ~sub & ~np.isnan(a)
+    if np.any(nrm):
+        frac, ex = np.frexp(a[nrm])       # a = frac * 2^ex, frac in [0.5, 1)
+        e = ex.astype(np.int64) - 1       # a = 2^e * f, f = 2 frac in [1, 2)
+        k = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)
+        carry = k == 8
+        e[carry] += 1
+        k[carry] = 0
+        codes[nrm] = ((e + 7) << 3) | k
+    codes[np.isnan(a)] = 0x7F
+    codes |= np.where(np.signbit(y), 0x80, 0)
+    return codes.astype(np.uint8)
+
+
+def quantize_e4m3fn(x, scale) -> np.ndarray:
+    """Per-tensor e4m3 storage of x with a float32 scale: bytes encode_e4m3fn(x / scale)."""
+    return encode_e4m3fn(np.asarray(x, dtype=np.float64) / np.float64(np.float32(scale)))
 
 
 def decode_e4m3fn(codes: np.ndarray, scale) -> np.ndarray:
@@ -198,14 +240,24 @@ def decode_layer(inp: dict, batch_ids=None, scale=SOFTMAX_SCALE):
     w = {n: to_f64(inp[n], ka) for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o")}
     c, c_hat, q = q_path(x, w["w_dq"], w["w_uq"], inp.get("eps", 1e-6), inp.get("gamma"))
     k_new, v_new = kv_project(x, w["w_k"], w["w_v"])
+    ks, vs = inp.get("k_scale"), inp.get("v_scale")
+    extra = {}
+    if kk == "fp8_e4m3":
+        # an e4m3 cache stores the appended rows quantized with the cache's
+        # per-tensor scales, and attention reads them back from the cache
+        k_codes, v_codes = quantize_e4m3fn(k_new, ks), quantize_e4m3fn(v_new, vs)
+        k_app, v_app = decode_e4m3fn(k_codes, ks), decode_e4m3fn(v_codes, vs)
+        extra = dict(k_new_codes=k_codes, v_new_codes=v_codes)
+    else:
+        k_app, v_app = k_new, v_new
     outs, lses = [], []
     for i, b in enumerate(ids):
         o0, n = int(inp["seq_off"][b]), int(inp["seq_len"][b])
-        kb = np.concatenate([to_f64(inp["k_cache"][o0:o0 + n], kk), k_new[i:i + 1]])
-        vb = np.concatenate([to_f64(inp["v_cache"][o0:o0 + n], kk), v_new[i:i + 1]])
+        kb = np.concatenate([to_f64(inp["k_cache"][o0:o0 + n], kk, ks), k_app[i:i + 1]])
+        vb = np.concatenate([to_f64(inp["v_cache"][o0:o0 + n], kk, vs), v_app[i:i + 1]])
         o, lse = attend_one(q[i], kb, vb, scale)
         outs.append(o)
         lses.append(lse)
     o = np.stack(outs)
     y = out_proj(o, w["w_o"])
-    return dict(c=c, c_hat=c_hat, q=q, k_new=k_new, v_new=v_new, o=o, lse=np.stack(lses), y=y)
+    return dict(c=c, c_hat=c_hat, q=q, k_new=k_new, v_new=v_new, o=o, lse=np.stack(lses), y=y, **extra)

@@ -90,6 +90,24 @@ def test_projections_reject_bad_arguments():
     assert kv(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_BF16,
               None) == mfa.MFA_ERR_INVALID_ARG
     assert kv(*args, 0, 2, mfa.MFA_BF16, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
+    k8 = mfa.raw_function("mfa_kv_append_fp8")
+    ok = dict(sk=0.01, sv=0.02, ws=FAKE, nbytes=1 << 30, B=2, dt=mfa.MFA_BF16)
+
+    def k8call(**kw):
+        a = dict(ok, **kw)
+        ptrs = [a.get(n, FAKE) for n in ("x", "wk", "wv", "kc", "vc", "off", "len")]
+        return k8(*ptrs, a["sk"], a["sv"], a["ws"], a["nbytes"], a["B"], a["dt"], None)
+
+    assert k8call(kc=None) == mfa.MFA_ERR_INVALID_ARG
+    assert k8call(B=0) == mfa.MFA_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-45):
+        assert k8call(sk=bad) == mfa.MFA_ERR_INVALID_ARG, bad
+        assert k8call(sv=bad) == mfa.MFA_ERR_INVALID_ARG, bad
+    assert k8call(dt=mfa.MFA_FP8_E4M3) == mfa.MFA_ERR_UNSUPPORTED
+    assert k8call(vc=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert k8call(off=FAKE + 4) == mfa.MFA_ERR_ALIGNMENT
+    assert k8call(ws=None) == mfa.MFA_ERR_WORKSPACE
+    assert k8call(nbytes=mfa.mfa_kv_append_workspace_size(2, mfa.MFA_BF16) - 1) == mfa.MFA_ERR_WORKSPACE
     op = mfa.raw_function("mfa_oproj")
     assert op(FAKE, FAKE, None, FAKE, 1 << 30, 2, mfa.MFA_BF16, None) == mfa.MFA_ERR_INVALID_ARG
     assert op(FAKE, FAKE, FAKE, FAKE, 1 << 30, 0, mfa.MFA_BF16, None) == mfa.MFA_ERR_INVALID_ARG

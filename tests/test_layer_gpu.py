@@ -7,6 +7,8 @@ oracle run from the stored inputs alone; "stage isolated" feeds the oracle's
 attention the GPU's own q and cache, so each kernel's error is seen alone.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -101,3 +103,87 @@ def test_layer_bf16_8k_full():
     print("[case] layer layer_bf16_8k (full size, sampled sequences)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_bf16_8k"])
     _check_layer(inp, [0, 77, 127], "bf16")
+
+
+# ------------------------------------------------------------------ e4m3 cache (quantize on append)
+def _check_codes(name, got, want, exact, scale):
+    """Appended e4m3 bytes against the oracle's. The GPU rounds its fp32
+    projection, the oracle the exact one, so a code may differ where the exact
+    value sits at a rounding midpoint; there the GPU's code must be as close to
+    the exact value as the oracle's, up to the fp32 accumulation error."""
+    t = om.e4m3fn_table()
+    got, want = np.asarray(got, dtype=np.uint8), np.asarray(want, dtype=np.uint8)
+    assert np.all(np.isfinite(t[got])), f"{name}: NaN code written"
+    same = got == want
+    y = np.asarray(exact, dtype=np.float64) / float(np.float32(scale))
+    dg, dw = np.abs(t[got] - y), np.abs(t[want] - y)
+    bad = ~same & (dg > dw + 1e-4 * np.abs(y) + 1e-6)
+    print(f"[parity] {name}: {int((~same).sum())} of {got.size} codes differ (all at rounding midpoints: "
+          f"{not bool(bad.any())})", flush=True)
+    assert not bad.any(), f"{name}: {int(bad.sum())} codes farther from the exact value than the oracle's"
+    assert same.mean() >= 0.99, f"{name}: only {same.mean():.4f} of the codes agree"
+
+
+def _check_layer_fp8(inp, ids, num_workgroups=0):
+    runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups)
+    t, tb = TOL["fp8_e4m3"], TOL["bf16"]
+    ref = om.decode_layer(inp, batch_ids=ids)
+    rows = (inp["seq_off"] + inp["seq_len"]).astype(np.int64)
+    sel = torch.as_tensor(rows[ids], device=dev["k"].device)
+    check("fp8 layer q", runner.to_f64(call.q)[ids], ref["q"], tb["atol"], tb["rel"])
+    _check_codes("fp8 layer k_new", dev["k"][sel].cpu().numpy(), ref["k_new_codes"], ref["k_new"], inp["k_scale"])
+    _check_codes("fp8 layer v_new", dev["v"][sel].cpu().numpy(), ref["v_new_codes"], ref["v_new"], inp["v_scale"])
+    # no other cache byte changed
+    mask = torch.ones(dev["k"].shape[0], dtype=torch.bool, device=dev["k"].device)
+    mask[torch.as_tensor(rows, device=mask.device)] = False
+    assert torch.equal(dev["k"][mask], k_before[mask]) and torch.equal(dev["v"][mask], v_before[mask])
+    check("fp8 layer o (end to end)", runner.to_f64(call.o)[ids], ref["o"], t["atol"], t["rel"])
+    check_lse("fp8 layer lse (end to end)", runner.to_f64(call.lse)[ids], ref["lse"], max(t["lse"], 5e-3))
+    check("fp8 layer y (end to end)", runner.to_f64(call.y)[ids], ref["y"], t["atol"], t["rel"])
+
+
+@pytest.mark.parametrize("G", [0, 3])
+def test_layer_fp8_cache_small(G):
+    print(f"[case] layer bf16 with e4m3 cache B=5 ctx=300 G={G}", flush=True)
+    w = gen.scaled(gen.WORKLOADS["layer_bf16_fp8kv_8k"], batch=5, ctx=300)
+    _check_layer_fp8(gen.make_layer(w), [0, 1, 2, 3, 4], num_workgroups=G)
+
+
+def test_layer_fp8_cache_full():
+    print("[case] layer layer_bf16_fp8kv_8k (full size, sampled sequences)", flush=True)
+    inp = gen.make_layer(gen.WORKLOADS["layer_bf16_fp8kv_8k"])
+    _check_layer_fp8(inp, [0, 64, 127])
+
+
+def test_kv_append_fp8_f32_activations_and_saturation():
+    # fp32 activations (the plain GEMM path) and a scale small enough that
+    # part of the row clamps at +-448
+    from decode_attention_attn_amd import mfa, runner
+
+    print("[case] kv_append_fp8 f32 activations, saturating scale", flush=True)
+    B, cap = 4, 5
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((B, 7168)).astype(np.float32)
+    w_k = (rng.standard_normal((256, 7168)) / math.sqrt(7168)).astype(np.float32)
+    w_v = (rng.standard_normal((256, 7168)) / math.sqrt(7168)).astype(np.float32)
+    off = np.arange(B, dtype=np.int64) * cap
+    lens = np.array([0, 3, 4, 1], dtype=np.int32)
+    kc = rng.integers(0, 0x7F, size=(B * cap, 256), dtype=np.uint8)
+    vc = rng.integers(0, 0x7F, size=(B * cap, 256), dtype=np.uint8)
+    sk, sv = np.float32(1.0 / 448), np.float32(3.0 / 448)  # |k| > 1 saturates
+    d = {n: runner.to_device(a, "f32") for n, a in (("x", x), ("wk", w_k), ("wv", w_v))}
+    dk, dv = runner.to_device(kc, "fp8_e4m3"), runner.to_device(vc, "fp8_e4m3")
+    doff, dlen = runner.to_device(off, "i64"), runner.to_device(lens, "i32")
+    ws = torch.empty(mfa.mfa_kv_append_workspace_size(B, mfa.MFA_F32), dtype=torch.uint8, device="cuda")
+    mfa.check(mfa.mfa_kv_append_fp8(d["x"], d["wk"], d["wv"], dk, dv, doff, dlen, sk, sv, ws, B, mfa.MFA_F32),
+              "mfa_kv_append_fp8")
+    torch.cuda.synchronize()
+    k_new, v_new = om.kv_project(x, w_k, w_v)
+    assert np.mean(np.abs(k_new / float(sk)) > 448) > 0.2  # the clamp is exercised
+    rows = off + lens
+    gk, gv = dk.cpu().numpy(), dv.cpu().numpy()
+    _check_codes("f32 k_new", gk[rows], om.quantize_e4m3fn(k_new, sk), k_new, sk)
+    _check_codes("f32 v_new", gv[rows], om.quantize_e4m3fn(v_new, sv), v_new, sv)
+    keep = np.ones(B * cap, dtype=bool)
+    keep[rows] = False
+    assert np.array_equal(gk[keep], kc[keep]) and np.array_equal(gv[keep], vc[keep])

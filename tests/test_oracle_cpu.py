@@ -90,6 +90,64 @@ def test_generator_e4m3_encoder_against_oracle_decoder():
     assert np.all(err == best)
 
 
+def test_oracle_e4m3_encoder_round_trips_every_code():
+    # encode(decode(c)) == c for all 254 finite codes, signed zeros included
+    t = om.e4m3fn_table()
+    finite = np.array([b for b in range(256) if not math.isnan(t[b])])
+    assert np.array_equal(om.encode_e4m3fn(t[finite]), finite.astype(np.uint8))
+    assert om.encode_e4m3fn(np.array([math.nan]))[0] & 0x7F == 0x7F
+
+
+def test_oracle_e4m3_encoder_ties_to_even_at_every_midpoint():
+    # the exact midpoint of two neighbouring codes goes to the one with an even
+    # mantissa (codes are ordered, so that is the even code); a hair either
+    # side goes to the nearer one
+    t = om.e4m3fn_table()
+    for c in range(0x00, 0x7E):
+        lo, hi = t[c], t[c + 1]
+        mid = (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert om.encode_e4m3fn(np.array([mid, -mid])).tolist() == [even, even | 0x80], hex(c)
+        eps = (hi - lo) * 1e-6
+        assert om.encode_e4m3fn(np.array([mid - eps, mid + eps])).tolist() == [c, c + 1], hex(c)
+
+
+def test_oracle_e4m3_encoder_saturates_and_flushes():
+    # beyond the largest finite magnitude the quantizer clamps to +-448
+    assert om.encode_e4m3fn(np.array([448.0, 460.0, 1e30, -500.0])).tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+    # below half the smallest subnormal (2^-10) a value rounds to zero, at it
+    # the tie goes to zero (even), above it to the smallest subnormal
+    assert om.encode_e4m3fn(np.array([2.0 ** -11, 2.0 ** -10, 2.0 ** -10 * 1.001])).tolist() == [0x00, 0x00, 0x01]
+    # the largest subnormal step carries into the smallest normal
+    assert om.encode_e4m3fn(np.array([2.0 ** -6 - 2.0 ** -11])).tolist() == [0x08]
+
+
+def test_oracle_e4m3_encoder_is_nearest_by_brute_force():
+    # against a search over the 254 finite values: nearest, ties to even
+    t = om.e4m3fn_table()
+    rng = np.random.default_rng(11)
+    mag = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 4000))
+    v = mag * rng.choice([-1.0, 1.0], mag.size)
+    got = om.encode_e4m3fn(v)
+    fin = np.array([b for b in range(256) if not math.isnan(t[b]) and b != 0x80])
+    d = np.abs(t[fin][None, :] - v[:, None])
+    best = d.min(axis=1)
+    for i in range(v.size):
+        cands = fin[d[i] == best[i]]
+        want = [c for c in cands if c % 2 == 0] if len(cands) > 1 else list(cands)
+        g = int(got[i])
+        if g in (0x00, 0x80):  # zero: either sign of the stored zero decodes to the nearest value 0
+            assert best[i] == abs(v[i]), v[i]
+            continue
+        assert g in want, (v[i], hex(g), [hex(c) for c in cands])
+
+
+def test_oracle_quantize_divides_by_the_float32_scale():
+    s = 0.1  # not a float32 value: the stored scale is float32(0.1)
+    x = np.array([0.3, -0.7, 5.0])
+    assert np.array_equal(om.quantize_e4m3fn(x, s), om.encode_e4m3fn(x / float(np.float32(s))))
+
+
 # ------------------------------------------------------------------ attention
 def _two_rows():
     g = {r[0]: [float(x) for x in r[1:]] for r in read_golden("attn_two_rows.txt")}
@@ -351,6 +409,43 @@ def _small_layer(seed=13, B=3, ctx=6):
         seq_len=np.full(B, ctx, dtype=np.int32),
     )
     return inp
+
+
+def _small_fp8_layer():
+    inp = _small_layer()
+    sk, sv = np.float32(4.0 / 448), np.float32(5.0 / 448)
+    kc, vc = om.quantize_e4m3fn(inp["k_cache"], sk), om.quantize_e4m3fn(inp["v_cache"], sv)
+    for b in range(3):
+        o0, n = int(inp["seq_off"][b]), int(inp["seq_len"][b])
+        kc[o0 + n:o0 + n + 2] = 0x7F  # free rows hold the NaN code
+        vc[o0 + n:o0 + n + 2] = 0x7F
+    return dict(inp, kind_kv="fp8_e4m3", k_cache=kc, v_cache=vc, k_scale=sk, v_scale=sv)
+
+
+def test_layer_fp8_cache_stores_the_new_rows_quantized():
+    inp = _small_fp8_layer()
+    out = om.decode_layer(inp)
+    assert np.all(np.isfinite(out["o"])) and np.all(np.isfinite(out["y"]))  # NaN free rows never read
+    # each new value is within half an e4m3 step of its code: 2^-4 relative in
+    # the normal range, 2^-10 (times the scale) among the subnormals
+    for new, codes, sc in ((out["k_new"], out["k_new_codes"], inp["k_scale"]),
+                           (out["v_new"], out["v_new_codes"], inp["v_scale"])):
+        err = np.abs(om.decode_e4m3fn(codes, sc) - new)
+        assert np.all(err <= np.maximum(np.abs(new) * 2.0 ** -4, 2.0 ** -10 * float(sc)) * (1 + 1e-12))
+        assert np.mean(err > 0) > 0.9  # quantization did happen
+    # zero K/V projections: the new row is stored as code 0 (value 0), so
+    # lse' = logaddexp(lse, 0) over the dequantized cached rows
+    z = dict(inp, w_k=np.zeros_like(inp["w_k"]), w_v=np.zeros_like(inp["w_v"]))
+    outz = om.decode_layer(z)
+    assert not np.any(outz["k_new_codes"] & 0x7F) and not np.any(outz["v_new_codes"] & 0x7F)
+    for b in range(3):
+        o0, n = int(inp["seq_off"][b]), int(inp["seq_len"][b])
+        kb = om.decode_e4m3fn(inp["k_cache"][o0:o0 + n], inp["k_scale"])
+        vb = om.decode_e4m3fn(inp["v_cache"][o0:o0 + n], inp["v_scale"])
+        oc, lc = om.attend_one(outz["q"][b], kb, vb)
+        ln = np.logaddexp(lc, 0.0)
+        assert np.allclose(outz["lse"][b], ln, atol=1e-12)
+        assert np.allclose(outz["o"][b], oc * np.exp(lc - ln)[:, None], atol=1e-12)
 
 
 def test_layer_attends_the_appended_row_and_nothing_beyond():
