@@ -7,8 +7,10 @@ already resident in HBM:
   * attention workloads (default ``attn_bf16_4k``: batch 32, 64 query heads
     over one shared bf16 K/V head, 4096 positions): one ``mfa_decode_attn``
     call, i.e. scores, online softmax, PV and the split merge;
-  * ``layer_bf16_8k`` / ``tiny_fp32``: the whole decode layer (q path, K/V
-    append, attention, out-projection).
+  * ``*_paged`` attention workloads: the same keys in a paged cache (64-row
+    pages in a shuffled order), one ``mfa_decode_attn_paged`` call;
+  * ``layer_bf16_8k`` / ``layer_bf16_fp8kv_8k`` / ``tiny_fp32``: the whole
+    decode layer (q path, K/V append, attention, out-projection).
 Prints one JSON line. ``value`` is KV-cache bytes read per second (GB/s) over
 the whole step; ``tokens_per_s`` is sequences decoded per second for this one
 layer. The K/V buffers rotate over several copies so that the 256 MB on-die
@@ -115,8 +117,11 @@ def bench_attn(name, steps, warmup, rotate, graph=True):
     from decode_attention_attn_amd import inputs as gen
     from decode_attention_attn_amd import runner
 
-    w = gen.WORKLOADS[name]
+    base, _, page = name.partition("_paged")
+    w = gen.WORKLOADS[base]
     inp = gen.make_attn(w)
+    if page:  # the same keys in 64-row pages, in a shuffled page order
+        inp = gen.to_pages(inp, 64, seed=1)
     dev = runner.upload_attn(inp)
     ks = [dev["k"]] + [dev["k"].clone() for _ in range(rotate - 1)]
     vs = [dev["v"]] + [dev["v"].clone() for _ in range(rotate - 1)]
@@ -197,8 +202,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn_bf16_4k",
-                    choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "layer_bf16_8k", "layer_bf16_fp8kv_8k",
-                             "tiny_fp32"])
+                    choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "attn_bf16_4k_paged",
+                             "attn_fp8kv_4k_paged", "layer_bf16_8k", "layer_bf16_fp8kv_8k", "tiny_fp32"])
     ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,7 +244,7 @@ def main():
     ms = res["ms"]
     gbps = res["kv_bytes"] / (ms * 1e-3) / 1e9
     achieved = res["alg_bytes"] / (ms * 1e-3) / 1e9
-    hbm_bytes = measured_traffic(w.name)
+    hbm_bytes = measured_traffic(res["workload"])
     line = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -254,7 +259,7 @@ def main():
         "dtype": "bf16" if w.act == "bf16" else "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name,
+            "workload": res["workload"],
             "batch": w.batch,
             "ctx": int(max(res["lengths"])),
             "q_heads": 64,
@@ -275,8 +280,9 @@ def main():
             # same call time as "achieved"; null when the kernel sources changed since the counters were taken
             "traffic": None if hbm_bytes is None else round(hbm_bytes / (ms * 1e-3) / 1e9, 2),
             "traffic_bytes_per_launch": hbm_bytes,
-            "kernel": "mfa_decode_attn call = attn_mfma_kernel + attn_combine_mfma_kernel (HIP events on the "
-            "call's stream)" if w.kind == "attn" else "whole layer (HIP events)",
+            "kernel": ("mfa_decode_attn_paged" if "_paged" in res["workload"] else "mfa_decode_attn")
+            + " call = attn_mfma_kernel + attn_combine_mfma_kernel (HIP events on the call's stream)"
+            if w.kind == "attn" else "whole layer (HIP events)",
             "alg_bytes_per_launch": res["alg_bytes"],
         },
     }

@@ -57,6 +57,9 @@ struct AttnArgs {
   void* part_o;     // [G + B][64][256] normalized partial outputs (bf16 for the MFMA kernels, fp32 otherwise)
   float* part_lse;  // [G + B][64] fp32, base-2 log-sum-exp of each partial
   int* meta;        // [B][2]: first partial slot and piece count of each sequence (0 pieces: written directly)
+  const int32_t* table;  // paged cache: [B][max_blocks] page of each page-sized block (null: contiguous)
+  int max_blocks;
+  int page_shift;        // page = 2^page_shift rows
   int B;
   int G;
   float score_mul;  // softmax_scale * k_scale * log2(e)
@@ -84,13 +87,22 @@ __device__ __forceinline__ int piece_index(int G) {
   return (G & 7) == 0 ? (i & 7) * (G >> 3) + (i >> 3) : i;
 }
 
+// A sequence's length in the work split. A paged cache pads every sequence
+// to a whole number of tiles, so that tiles (multiples of kRows from the
+// sequence's first row) never straddle a page; the padding rows are masked.
+template <int kRows, bool PAGED>
+__device__ __forceinline__ long long split_len(long long len) {
+  return PAGED ? (len + kRows - 1) / kRows * kRows : len;
+}
+
 // Walks one workgroup's piece tile by tile (wave-uniform state).
-template <int kRows>
+template <int kRows, bool PAGED = false>
 struct Cursor {
   long long gpos, r1;            // next global position, end of the workgroup's piece
   long long per;                 // piece length (rows per workgroup)
   long long seq_start, seq_end;  // global range of the current sequence
-  long long off;                 // cache row of the sequence's first key
+  long long off;                 // cache row of the sequence's first key (contiguous cache)
+  long long len;                 // the sequence's length (seq_end - seq_start less the paging pad)
   int b;
 
   __device__ __forceinline__ bool valid() const { return gpos < r1; }
@@ -107,13 +119,20 @@ struct Cursor {
     const long long e = gpos + kRows;
     gpos = e < pe ? e : pe;
     if (gpos == seq_end && gpos < r1) {
+      long long n;
       do {
         ++b;
         seq_start = seq_end;
-        seq_end = seq_start + load_scalar(len, b);
+        n = load_scalar(len, b);
+        seq_end = seq_start + split_len<kRows, PAGED>(n);
       } while (seq_end == seq_start);
-      off = load_scalar(offs, b);
+      this->len = n;
+      if (!PAGED) off = load_scalar(offs, b);
     }
+  }
+  // rows of the current tile that hold keys
+  __device__ __forceinline__ int valid_rows(long long lo, long long hi) const {
+    return (int)((PAGED && hi > len ? len : hi) - lo);
   }
 };
 
@@ -123,14 +142,15 @@ struct Cursor {
 // not yet in the instruction cache and every fetch of it queues behind the
 // tile loads of the workgroups that got going first. The first 64 sequences
 // stay in registers; more are re-read chunk by chunk.
-template <int kRows>
-__device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane, Cursor<kRows>& c) {
+template <int kRows, bool PAGED>
+__device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane, Cursor<kRows, PAGED>& c) {
   const int B = a.B;
   const int ic = lane < B ? lane : B - 1;
-  const long long v0 = lane < B ? (long long)a.seq_len[ic] : 0;
-  const long long o0 = a.seq_off[ic];
+  const long long n0 = lane < B ? (long long)a.seq_len[ic] : 0;
+  const long long v0 = split_len<kRows, PAGED>(n0);
+  const long long o0 = PAGED ? 0 : a.seq_off[ic];
   long long sum = v0;
-  for (int i = 64 + lane; i < B; i += 64) sum += a.seq_len[i];
+  for (int i = 64 + lane; i < B; i += 64) sum += split_len<kRows, PAGED>(a.seq_len[i]);
   const long long total = uniform(wave_sum_ll(sum));
   const long long per = piece_len(total, a.G);
   const long long r0 = (long long)wgi * per;
@@ -138,7 +158,8 @@ __device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane
   long long base = 0;
   for (int c0 = 0; c0 < B; c0 += 64) {
     const int i = c0 + lane;
-    const long long v = c0 == 0 ? v0 : (i < B ? (long long)a.seq_len[i] : 0);
+    const long long n = c0 == 0 ? n0 : (i < B ? (long long)a.seq_len[i] : 0);
+    const long long v = split_len<kRows, PAGED>(n);
     long long incl = v;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -156,7 +177,8 @@ __device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane
       c.b = b;
       c.seq_start = start;
       c.seq_end = start + uniform(__shfl(v, first));
-      c.off = c0 == 0 ? uniform(__shfl(o0, first)) : load_scalar(a.seq_off, b);
+      c.len = uniform(__shfl(n, first));
+      c.off = PAGED ? 0 : (c0 == 0 ? uniform(__shfl(o0, first)) : load_scalar(a.seq_off, b));
       return true;
     }
     base += __shfl(incl, 63);
@@ -190,15 +212,24 @@ __device__ __forceinline__ int swz_v8(int r) { return (r & 3) | (((r >> 4) & 1) 
 // applied on the global side: slot (row r, chunk pc) receives global chunk
 // pc ^ swz(r). Each row is still read as one full run. Rows past the valid
 // end re-read the last valid row (their scores are masked to -inf).
-template <bool FP8>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<FP8>::kRows>& c, char* stage, int w,
-                                           int lane) {
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<FP8>::kRows, PAGED>& c, char* stage,
+                                           int w, int lane) {
   using C = Cfg<FP8>;
   long long lo, hi;
   c.tile(lo, hi);
-  const char* kb = (const char*)a.k + (c.off + lo) * C::kRowBytes;
-  const char* vb = (const char*)a.v + (c.off + lo) * C::kRowBytes;
-  const int nvalid = (int)(hi - lo);
+  long long row0;  // cache row of the tile's first key
+  if constexpr (PAGED) {
+    // the tile lies inside one page (tiles start at multiples of kRows, a
+    // page holds a whole number of tiles): one table entry per tile
+    const long long page = load_scalar(a.table, (long long)c.b * a.max_blocks + (lo >> a.page_shift));
+    row0 = (page << a.page_shift) + (lo & ((1LL << a.page_shift) - 1));
+  } else {
+    row0 = c.off + lo;
+  }
+  const char* kb = (const char*)a.k + row0 * C::kRowBytes;
+  const char* vb = (const char*)a.v + row0 * C::kRowBytes;
+  const int nvalid = c.valid_rows(lo, hi);
   const int r_in = lane / C::kChunksPerRow;
   const int pc = lane % C::kChunksPerRow;
 #pragma unroll
@@ -483,7 +514,7 @@ __device__ __forceinline__ void attend_tile_fp8(const char* ks, const char* vs, 
   softmax_pv(b0, b1, nvalid - 32, g, score_mul, vf, m_run, l_run, acc);
 }
 
-template <bool FP8>
+template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   using C = Cfg<FP8>;
   // the 4-stage tile ring, then q (32 KB): 160 KB of LDS
@@ -495,9 +526,9 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   const int g = lane >> 4;
   const int wgi = piece_index(a.G);
 
-  Cursor<C::kRows> prod;
+  Cursor<C::kRows, PAGED> prod;
   if (!init_cursor(a, wgi, lane, prod)) return;
-  Cursor<C::kRows> cons = prod;
+  Cursor<C::kRows, PAGED> cons = prod;
 
   // q of the first piece goes out ahead of the first tile DMAs.
   issue_q(a, cons.b, qs, w, lane);
@@ -505,7 +536,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s) {
     if (prod.valid()) {
-      issue_tile<FP8>(a, prod, ring + s * C::kTileBytes, w, lane);
+      issue_tile<FP8, PAGED>(a, prod, ring + s * C::kTileBytes, w, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
@@ -554,14 +585,14 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     drained = false;
     __builtin_amdgcn_s_barrier();
     if (prod.valid()) {
-      issue_tile<FP8>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, w, lane);
+      issue_tile<FP8, PAGED>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, w, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
     char* stage = ring + (t % C::kStages) * C::kTileBytes;
     long long lo, hi;
     cons.tile(lo, hi);
-    const int nvalid = (int)(hi - lo);
+    const int nvalid = cons.valid_rows(lo, hi);
     if constexpr (FP8)
       attend_tile_fp8(stage, stage + C::kHalfBytes, nvalid, n, g, vr, q8, a.score_mul, m_run, l_run, acc);
     else
@@ -866,6 +897,9 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
   a.part_o = p.ws;
   a.part_lse = (float*)((char*)p.ws + attn_part_o_bytes(p.B, p.G));
   a.meta = (int*)((char*)p.ws + attn_meta_offset(p.B, p.G));
+  a.table = p.table;
+  a.max_blocks = p.max_blocks;
+  a.page_shift = p.page_shift;
   a.B = p.B;
   a.G = p.G;
   a.score_mul = p.softmax_scale * p.k_scale * kLog2e;
@@ -880,11 +914,13 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
       if (e == hipSuccess) e = launch(attn_combine_f32_kernel, comb_f32, block, stream, a);
       break;
     case AttnKind::BF16:
-      e = launch(attn_mfma_kernel<false>, dim3(p.G), block, stream, a);
+      e = p.table ? launch(attn_mfma_kernel<false, true>, dim3(p.G), block, stream, a)
+                  : launch(attn_mfma_kernel<false, false>, dim3(p.G), block, stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
-      e = launch(attn_mfma_kernel<true>, dim3(p.G), block, stream, a);
+      e = p.table ? launch(attn_mfma_kernel<true, true>, dim3(p.G), block, stream, a)
+                  : launch(attn_mfma_kernel<true, false>, dim3(p.G), block, stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
   }

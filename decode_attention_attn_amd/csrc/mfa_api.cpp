@@ -221,16 +221,25 @@ size_t mfa_decode_attn_workspace_size(int B, int num_workgroups) {
   return mfa::attn_ws_bytes(B, G);
 }
 
-int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
-                    const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale, void* out, float* lse,
-                    void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
-                    void* stream) {
-  if (!q || !k_cache || !v_cache || !seq_off || !seq_len || !out || B < 1 || B > MFA_MAX_BATCH ||
+// Shared by the contiguous and the paged entry points (table == null: contiguous).
+static int decode_attn_impl(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                            const int32_t* block_table, int max_blocks, int page_rows, const int32_t* seq_len,
+                            float softmax_scale, float k_scale, float v_scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
+                            void* stream) {
+  const bool paged = block_table != nullptr;
+  if (!q || !k_cache || !v_cache || (!paged && !seq_off) || !seq_len || !out || B < 1 || B > MFA_MAX_BATCH ||
       num_workgroups < 0 || num_workgroups > 65536 || !isfinite(softmax_scale) || !isfinite(k_scale) ||
       !isfinite(v_scale))
     return MFA_ERR_INVALID_ARG;
+  int page_shift = 0;
+  if (paged) {
+    if (max_blocks < 1 || page_rows < 64 || page_rows > (1 << 20) || (page_rows & (page_rows - 1)) != 0)
+      return MFA_ERR_INVALID_ARG;
+    while ((1 << page_shift) < page_rows) ++page_shift;
+  }
   mfa::AttnKind kind;
-  if (q_dt == MFA_F32 && kv_dt == MFA_F32)
+  if (q_dt == MFA_F32 && kv_dt == MFA_F32 && !paged)
     kind = mfa::AttnKind::F32;
   else if (q_dt == MFA_BF16 && kv_dt == MFA_BF16)
     kind = mfa::AttnKind::BF16;
@@ -239,7 +248,8 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
   else
     return MFA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws) ||
-      !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) || (lse && !aligned_n(lse, 4)))
+      (!paged && !aligned_n(seq_off, 8)) || (paged && !aligned_n(block_table, 4)) || !aligned_n(seq_len, 4) ||
+      (lse && !aligned_n(lse, 4)))
     return MFA_ERR_ALIGNMENT;
   if (!ws) return MFA_ERR_WORKSPACE;
   int G = num_workgroups;
@@ -264,7 +274,28 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
   p.softmax_scale = softmax_scale;
   p.k_scale = kind == mfa::AttnKind::BF16_FP8KV ? k_scale : 1.f;
   p.v_scale = kind == mfa::AttnKind::BF16_FP8KV ? v_scale : 1.f;
+  p.table = block_table;
+  p.max_blocks = paged ? max_blocks : 0;
+  p.page_shift = page_shift;
   return hip_status(mfa::launch_decode_attn(p, (hipStream_t)stream));
+}
+
+int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                    const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale, void* out, float* lse,
+                    void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
+                    void* stream) {
+  if (!seq_off) return MFA_ERR_INVALID_ARG;
+  return decode_attn_impl(q, k_cache, v_cache, seq_off, nullptr, 0, 0, seq_len, softmax_scale, k_scale, v_scale,
+                          out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt, stream);
+}
+
+int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                          int max_blocks, int page_rows, const int32_t* seq_len, float softmax_scale, float k_scale,
+                          float v_scale, void* out, float* lse, void* ws, size_t ws_bytes, int B,
+                          int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream) {
+  if (!block_table) return MFA_ERR_INVALID_ARG;
+  return decode_attn_impl(q, k_pages, v_pages, nullptr, block_table, max_blocks, page_rows, seq_len, softmax_scale,
+                          k_scale, v_scale, out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt, stream);
 }
 
 // ------------------------------------------------------------------ out-projection

@@ -41,6 +41,10 @@ struct AttnLaunch {
   int B;
   int G;  // workgroups of the main kernel
   float softmax_scale, k_scale, v_scale;
+  // paged cache (MFMA kinds only): null table = contiguous rows at seq_off
+  const int32_t* table = nullptr;
+  int max_blocks = 0;
+  int page_shift = 0;
 };
 
 // Workspace: partial outputs [G + B][64][256] (fp32-sized; bf16 partials use

@@ -37,7 +37,7 @@ HEAD_DIM = 256
 QDIM = N_HEADS * HEAD_DIM  # 16384
 
 # Stream ids, one per tensor.
-ID_X, ID_WDQ, ID_WUQ, ID_WK, ID_WV, ID_WO, ID_Q, ID_K, ID_V, ID_LEN = range(10)
+ID_X, ID_WDQ, ID_WUQ, ID_WK, ID_WV, ID_WO, ID_Q, ID_K, ID_V, ID_LEN, ID_PAGES = range(11)
 
 F32, BF16, FP8 = "f32", "bf16", "fp8_e4m3"
 
@@ -219,6 +219,38 @@ def make_attn(w: Workload, lengths: Optional[np.ndarray] = None) -> dict:
     v, v_scale = _kv_store(normal(w.seed, ID_V, (max(rows, 1), HEAD_DIM)), w.kv)
     return dict(workload=w, q=q, k_cache=k, v_cache=v, k_scale=k_scale, v_scale=v_scale,
                 seq_off=off, seq_len=lengths, kind_q=w.act, kind_kv=w.kv)
+
+
+def to_pages(inp: dict, page_rows: int, seed: int = 0, spare_pages: int = 3) -> dict:
+    """Paged copy of attention inputs from ``make_attn``: the same keys and
+    values, with each sequence's rows cut into blocks of ``page_rows`` and the
+    blocks placed on pages in a seeded random order (plus a few unused pages).
+    Rows of a sequence's last page past its length, and the unused pages,
+    hold NaN codes (bf16 0x7FC0, fp32 NaN, e4m3 0x7F): a read of them shows.
+    Unused table entries point at page 0."""
+    lens = np.asarray(inp["seq_len"], dtype=np.int64)
+    off = np.asarray(inp["seq_off"], dtype=np.int64)
+    nblk = (lens + page_rows - 1) // page_rows
+    n_pages = int(nblk.sum()) + spare_pages
+    max_blocks = max(int(nblk.max()), 1)
+    perm = np.random.default_rng([seed, ID_PAGES]).permutation(n_pages)
+    table = np.zeros((len(lens), max_blocks), dtype=np.int32)
+    kind = inp["kind_kv"]
+    fill = {F32: np.float32(np.nan), BF16: np.uint16(0x7FC0), FP8: np.uint8(0x7F)}[kind]
+    kc, vc = inp["k_cache"], inp["v_cache"]
+    kp = np.full((n_pages * page_rows,) + kc.shape[1:], fill, dtype=kc.dtype)
+    vp = np.full((n_pages * page_rows,) + vc.shape[1:], fill, dtype=vc.dtype)
+    nxt = 0
+    for b in range(len(lens)):
+        for j in range(int(nblk[b])):
+            page = int(perm[nxt])
+            nxt += 1
+            table[b, j] = page
+            n = int(min(page_rows, lens[b] - j * page_rows))
+            src = int(off[b]) + j * page_rows
+            kp[page * page_rows:page * page_rows + n] = kc[src:src + n]
+            vp[page * page_rows:page * page_rows + n] = vc[src:src + n]
+    return dict(inp, k_pages=kp, v_pages=vp, block_table=table, max_blocks=max_blocks, page_rows=page_rows)
 
 
 CANARY = 1234.0  # value left in cache rows that the step must not read before writing

@@ -56,13 +56,20 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 def upload_attn(inp: dict, device="cuda") -> dict:
+    """Attention inputs on the device; a paged layout (``inputs.to_pages``)
+    uploads the pages and the block table instead of the packed cache."""
+    paged = "block_table" in inp
+    kk = inp["kind_kv"]
     return dict(
         q=to_device(inp["q"], inp["kind_q"], device),
-        k=to_device(inp["k_cache"], inp["kind_kv"], device),
-        v=to_device(inp["v_cache"], inp["kind_kv"], device),
+        k=to_device(inp["k_pages"] if paged else inp["k_cache"], kk, device),
+        v=to_device(inp["v_pages"] if paged else inp["v_cache"], kk, device),
         off=to_device(inp["seq_off"], "i64", device),
         len=to_device(inp["seq_len"], "i32", device),
-        kind_q=inp["kind_q"], kind_kv=inp["kind_kv"],
+        table=to_device(inp["block_table"], "i32", device) if paged else None,
+        max_blocks=int(inp["max_blocks"]) if paged else 0,
+        page_rows=int(inp["page_rows"]) if paged else 0,
+        kind_q=inp["kind_q"], kind_kv=kk,
         k_scale=float(inp["k_scale"]) if inp["k_scale"] is not None else 1.0,
         v_scale=float(inp["v_scale"]) if inp["v_scale"] is not None else 1.0,
         B=len(inp["seq_len"]),
@@ -84,10 +91,18 @@ class AttnCall:
 
     def __call__(self, k=None, v=None):
         d = self.dev
-        st = mfa.mfa_decode_attn(d["q"], d["k"] if k is None else k, d["v"] if v is None else v, d["off"], d["len"],
-                                 SOFTMAX_SCALE, d["k_scale"], d["v_scale"], self.out, self.lse, self.ws, d["B"],
-                                 self.G, _DT[d["kind_q"]], _DT[d["kind_kv"]], self.stream)
-        mfa.check(st, "mfa_decode_attn")
+        k = d["k"] if k is None else k
+        v = d["v"] if v is None else v
+        if d.get("table") is not None:
+            st = mfa.mfa_decode_attn_paged(d["q"], k, v, d["table"], d["max_blocks"], d["page_rows"], d["len"],
+                                           SOFTMAX_SCALE, d["k_scale"], d["v_scale"], self.out, self.lse, self.ws,
+                                           d["B"], self.G, _DT[d["kind_q"]], _DT[d["kind_kv"]], self.stream)
+            mfa.check(st, "mfa_decode_attn_paged")
+        else:
+            st = mfa.mfa_decode_attn(d["q"], k, v, d["off"], d["len"], SOFTMAX_SCALE, d["k_scale"], d["v_scale"],
+                                     self.out, self.lse, self.ws, d["B"], self.G, _DT[d["kind_q"]],
+                                     _DT[d["kind_kv"]], self.stream)
+            mfa.check(st, "mfa_decode_attn")
         return self.out, self.lse
 
 

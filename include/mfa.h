@@ -141,6 +141,27 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
                     void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups,
                     mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
 
+/* ------------------------------------------------------------------ attention, paged cache
+ * mfa_decode_attn over a paged cache: sequence b's rows live in fixed-size
+ * pages of page_rows rows, its j-th block of page_rows keys (rows
+ * j*page_rows .. j*page_rows + page_rows - 1 of the sequence) in page
+ * block_table[b * max_blocks + j], which occupies rows
+ * page*page_rows .. page*page_rows + page_rows - 1 of k_pages / v_pages
+ * ([n_pages * page_rows, 256], kv_dt). Everything else (the computation,
+ * scales, outputs, lse, num_workgroups, workspace size) is as for
+ * mfa_decode_attn; the same workspace size applies. Supported (q_dt, kv_dt):
+ * (BF16, BF16), (BF16, FP8_E4M3). page_rows: a power of two, 64 <= page_rows
+ * <= 2^20; max_blocks >= 1 (else MFA_ERR_INVALID_ARG); block_table int32,
+ * 4-byte aligned. Device-side precondition: seq_len[b] <= max_blocks *
+ * page_rows and the first ceil(seq_len[b] / page_rows) entries of row b are
+ * valid pages (rows past seq_len[b] are never used as keys).
+ */
+int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, int max_blocks, int page_rows,
+                          const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale,
+                          void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups,
+                          mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
+
 /* ------------------------------------------------------------------ out-projection
  * y = O_flat W_o^T: attn [B, 16384] (the [B, 64, 256] attention output),
  * W_o [7168, 16384], y [B, 7168]. dt = MFA_F32 or MFA_BF16 (fp32 accumulation).

@@ -29,6 +29,9 @@ Readings where the pages are silent (each one is a choice this library makes):
     appended in this step included; no mask;
   * log-sum-exp uses the natural log; a sequence with no rows gives output 0
     and lse = -inf;
+  * a paged cache holds sequence b's keys j*R .. j*R + R - 1 (R rows per
+    page) on page block_table[b][j]; it is the same sequence of keys, laid
+    out in pages (the pages give no layout; paging is a serving choice);
   * an fp8 cache is OCP E4M3 ("fn") bytes with one float32 scale per tensor
     (the model runs in FP8, attention included: Step-3 summary, "Key
     claims"); a new row is stored as e4m3(x / scale), rounded to nearest with
@@ -212,6 +215,34 @@ def decode_attn(q, k_cache, v_cache, seq_off, seq_len, scale=SOFTMAX_SCALE,
         kb = up(k_cache[o0:o0 + n], kind_kv, k_scale)
         vb = up(v_cache[o0:o0 + n], kind_kv, v_scale)
         o, lse = attend_one(qb, kb, vb, scale)
+        outs.append(o)
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+def paged_rows(block_table_row, n, page_rows):
+    """Cache rows of a paged sequence's first n keys: key j sits in block
+    j // page_rows, i.e. on page block_table_row[j // page_rows], at row
+    page * page_rows + j % page_rows."""
+    j = np.arange(int(n), dtype=np.int64)
+    pages = np.asarray(block_table_row, dtype=np.int64)[j // page_rows]
+    return pages * page_rows + j % page_rows
+
+
+def decode_attn_paged(q, k_pages, v_pages, block_table, seq_len, page_rows, scale=SOFTMAX_SCALE,
+                      kind_q="f64", kind_kv="f64", k_scale=None, v_scale=None, batch_ids=None):
+    """decode_attn over a paged cache: each sequence's keys are gathered from
+    its pages in block order, then attended exactly as a contiguous run."""
+    ids = range(len(seq_len)) if batch_ids is None else batch_ids
+
+    def up(a, kind, sc):
+        return np.asarray(a, dtype=np.float64) if kind == "f64" else to_f64(a, kind, sc)
+
+    outs, lses = [], []
+    for b in ids:
+        rows = paged_rows(block_table[b], seq_len[b], page_rows)
+        o, lse = attend_one(up(q[b], kind_q, None), up(k_pages[rows], kind_kv, k_scale),
+                            up(v_pages[rows], kind_kv, v_scale), scale)
         outs.append(o)
         lses.append(lse)
     return np.stack(outs), np.stack(lses)

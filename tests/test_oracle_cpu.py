@@ -280,6 +280,36 @@ def test_any_partition_merges_back_by_lse():
     assert np.allclose(m + np.log(wts.sum(axis=0)), lse, atol=1e-12)
 
 
+def test_paged_rows_by_hand():
+    # page 5 then page 2, 4 rows per page: keys 0..3 -> rows 20..23, keys 4..5 -> rows 8..9
+    assert om.paged_rows([5, 2, 9], 6, 4).tolist() == [20, 21, 22, 23, 8, 9]
+    assert om.paged_rows([7], 0, 64).tolist() == []
+
+
+def test_paged_attention_equals_the_contiguous_layout():
+    # the same keys in shuffled pages (NaN in every row not holding a key)
+    # give the contiguous result exactly; a key row moved to the wrong page
+    # or an unread tail would change or poison it
+    rng = np.random.default_rng(4)
+    lens = np.array([1, 7, 8, 9, 0, 20], dtype=np.int32)
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    q = rng.standard_normal((len(lens), 4, 16))
+    k = rng.standard_normal((max(int(lens.sum()), 1), 16))
+    v = rng.standard_normal((max(int(lens.sum()), 1), 16))
+    inp = dict(q=q, k_cache=k, v_cache=v, seq_off=off, seq_len=lens, kind_kv="f32")
+    pg = gen.to_pages(inp, 8, seed=3)
+    assert np.isnan(pg["k_pages"]).any()  # unused rows are poisoned
+    o_c, l_c = om.decode_attn(q, k, v, off, lens, scale=0.25)
+    o_p, l_p = om.decode_attn_paged(q, pg["k_pages"], pg["v_pages"], pg["block_table"], lens, 8, scale=0.25)
+    assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
+    # brute force on one sequence straight from the pages
+    b = 5
+    rows = [int(pg["block_table"][b][j // 8]) * 8 + j % 8 for j in range(int(lens[b]))]
+    kr, vr = pg["k_pages"][rows].tolist(), pg["v_pages"][rows].tolist()
+    bo, bl = brute.mha(q[b].tolist(), [kr] * 4, [vr] * 4, 0.25)
+    assert np.allclose(o_p[b], bo, atol=1e-12) and np.allclose(l_p[b], bl, atol=1e-12)
+
+
 def test_empty_sequence_gives_zero_and_minus_inf():
     o, lse = om.attend_one(np.ones((64, 256)), np.zeros((0, 256)), np.zeros((0, 256)))
     assert np.all(o == 0) and np.all(np.isneginf(lse))
