@@ -9,6 +9,9 @@ already resident in HBM:
     call, i.e. scores, online softmax, PV and the split merge;
   * ``*_paged`` attention workloads: the same keys in a paged cache (64-row
     pages in a shuffled order), one ``mfa_decode_attn_paged`` call;
+  * ``*_mtp2`` attention workloads: two new query tokens per sequence
+    (causal between them), one ``mfa_decode_attn_mt`` call; tokens/s counts
+    both;
   * ``layer_bf16_8k`` / ``layer_bf16_fp8kv_8k`` / ``tiny_fp32``: the whole
     decode layer (q path, K/V append, attention, out-projection).
 Prints one JSON line. ``value`` is KV-cache bytes read per second (GB/s) over
@@ -117,11 +120,14 @@ def bench_attn(name, steps, warmup, rotate, graph=True):
     from decode_attention_attn_amd import inputs as gen
     from decode_attention_attn_amd import runner
 
-    base, _, page = name.partition("_paged")
+    base = name.replace("_paged", "").replace("_mtp2", "")
     w = gen.WORKLOADS[base]
     inp = gen.make_attn(w)
-    if page:  # the same keys in 64-row pages, in a shuffled page order
+    if "_paged" in name:  # the same keys in 64-row pages, in a shuffled page order
         inp = gen.to_pages(inp, 64, seed=1)
+    nt = 2 if "_mtp2" in name else 1
+    if nt > 1:  # two new query tokens per sequence, causal between them
+        inp = gen.with_tokens(inp, nt)
     dev = runner.upload_attn(inp)
     ks = [dev["k"]] + [dev["k"].clone() for _ in range(rotate - 1)]
     vs = [dev["v"]] + [dev["v"].clone() for _ in range(rotate - 1)]
@@ -132,8 +138,9 @@ def bench_attn(name, steps, warmup, rotate, graph=True):
                             graph_calls=4 * rotate if graph else 0)
     B = w.batch
     kv = _kv_bytes(inp["seq_len"], w.kv)
-    qo = 2 * B * 64 * 256 * (4 if w.act == "f32" else 2)
-    return dict(workload=name, ms=ms, B=B, kv_bytes=kv, alg_bytes=kv + qo, lengths=inp["seq_len"], inp=inp, w=w)
+    qo = 2 * nt * B * 64 * 256 * (4 if w.act == "f32" else 2)
+    return dict(workload=name, ms=ms, B=B, tokens=B * nt, kv_bytes=kv, alg_bytes=kv + qo, lengths=inp["seq_len"],
+                inp=inp, w=w)
 
 
 def bench_layer(name, steps, warmup, graph=True):
@@ -174,7 +181,13 @@ def cpu_baseline(res, seconds):
     done_seqs, done_kv, t0 = 0, 0, time.perf_counter()
     b = 0
     while time.perf_counter() - t0 < seconds:
-        if w.kind == "attn":
+        nt = int(inp.get("n_tokens", 1))
+        if w.kind == "attn" and nt > 1:
+            om.decode_attn_mt(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_off"], inp["seq_len"], nt,
+                              kind_q=inp["kind_q"], kind_kv=inp["kind_kv"], k_scale=inp["k_scale"],
+                              v_scale=inp["v_scale"], batch_ids=[b])
+            done_kv += _kv_bytes([inp["seq_len"][b]], w.kv)
+        elif w.kind == "attn":
             om.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_off"], inp["seq_len"],
                            kind_q=inp["kind_q"], kind_kv=inp["kind_kv"], k_scale=inp["k_scale"],
                            v_scale=inp["v_scale"], batch_ids=[b])
@@ -182,7 +195,7 @@ def cpu_baseline(res, seconds):
         else:
             om.decode_layer(inp, batch_ids=[b])
             done_kv += _kv_bytes([inp["seq_len"][b] + 1], w.kv)
-        done_seqs += 1
+        done_seqs += nt
         b = (b + 1) % B
     dt = time.perf_counter() - t0
     return {
@@ -203,7 +216,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn_bf16_4k",
                     choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "attn_bf16_4k_paged",
-                             "attn_fp8kv_4k_paged", "layer_bf16_8k", "layer_bf16_fp8kv_8k", "tiny_fp32"])
+                             "attn_fp8kv_4k_paged", "attn_bf16_4k_mtp2", "attn_fp8kv_4k_mtp2", "layer_bf16_8k",
+                             "layer_bf16_fp8kv_8k", "tiny_fp32"])
     ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -268,7 +282,7 @@ def main():
             "kv_dtype": w.kv,
             "kv_buffer_sets": args.rotate if w.kind == "attn" else 1,
         },
-        "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "tokens_per_s": round(res.get("tokens", w.batch) / (ms * 1e-3), 1),
         "pct_of_peak_hbm": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
@@ -280,7 +294,8 @@ def main():
             # same call time as "achieved"; null when the kernel sources changed since the counters were taken
             "traffic": None if hbm_bytes is None else round(hbm_bytes / (ms * 1e-3) / 1e9, 2),
             "traffic_bytes_per_launch": hbm_bytes,
-            "kernel": ("mfa_decode_attn_paged" if "_paged" in res["workload"] else "mfa_decode_attn")
+            "kernel": ("mfa_decode_attn_paged" if "_paged" in res["workload"] else
+                       "mfa_decode_attn_mt" if "_mtp2" in res["workload"] else "mfa_decode_attn")
             + " call = attn_mfma_kernel + attn_combine_mfma_kernel (HIP events on the call's stream)"
             if w.kind == "attn" else "whole layer (HIP events)",
             "alg_bytes_per_launch": res["alg_bytes"],

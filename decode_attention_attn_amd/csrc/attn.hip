@@ -60,6 +60,7 @@ struct AttnArgs {
   const int32_t* table;  // paged cache: [B][max_blocks] page of each page-sized block (null: contiguous)
   int max_blocks;
   int page_shift;        // page = 2^page_shift rows
+  int nt;                // new query tokens per sequence (1 or 2)
   int B;
   int G;
   float score_mul;  // softmax_scale * k_scale * log2(e)
@@ -188,7 +189,10 @@ __device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane
 
 // ---------------------------------------------------------------------------
 // MFMA kernel (bf16 q; bf16 or fp8 cache).
-template <bool FP8>
+// NT = new query tokens per sequence (1, or 2 for multi-token decode): wave w
+// serves token w / 4, heads 16 (w % 4)..+15, so NT tokens take 4 NT waves,
+// and their q (32 KB each) sit beside the ring.
+template <bool FP8, int NT = 1>
 struct Cfg {
   static constexpr int kRowBytes = FP8 ? 256 : 512;
   static constexpr int kRows = FP8 ? 64 : 32;                     // cache rows per tile
@@ -196,10 +200,12 @@ struct Cfg {
   static constexpr int kTileBytes = 2 * kHalfBytes;                // 32 KB
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;           // rows per 1 KB DMA block
-  static constexpr int kBlocksPerWave = kHalfBytes / 1024 / 4;     // DMA blocks per wave per half: 4
-  static constexpr int kDmaPerWave = 2 * kBlocksPerWave;           // DMA instructions per wave per tile: 8
-  static constexpr int kStages = 4;                                // LDS ring: 3 tiles in flight
-  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;    // DMAs still in flight once a tile landed
+  static constexpr int kWaves = 4 * NT;
+  static constexpr int kBlocksPerWave = kHalfBytes / 1024 / kWaves;  // DMA blocks per wave per half: 4 (2)
+  static constexpr int kDmaPerWave = 2 * kBlocksPerWave;             // DMA instructions per wave per tile: 8 (4)
+  static constexpr int kStages = NT == 1 ? 4 : 3;                    // LDS ring: 3 (2) tiles in flight
+  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;      // DMAs still in flight once a tile landed
+  static constexpr int kLdsBytes = kStages * kTileBytes + NT * kHeads * kHeadDim * 2;  // 160 KB
 };
 
 // XOR swizzles of 16-byte chunks within a row (row r = 0..31 of a 32-row block).
@@ -212,10 +218,10 @@ __device__ __forceinline__ int swz_v8(int r) { return (r & 3) | (((r >> 4) & 1) 
 // applied on the global side: slot (row r, chunk pc) receives global chunk
 // pc ^ swz(r). Each row is still read as one full run. Rows past the valid
 // end re-read the last valid row (their scores are masked to -inf).
-template <bool FP8, bool PAGED>
+template <bool FP8, bool PAGED, int NT>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<FP8>::kRows, PAGED>& c, char* stage,
                                            int w, int lane) {
-  using C = Cfg<FP8>;
+  using C = Cfg<FP8, NT>;
   long long lo, hi;
   c.tile(lo, hi);
   long long row0;  // cache row of the tile's first key
@@ -251,11 +257,13 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
 // the cache tiles: it is then tracked by the same wait counts, so the
 // prologue can wait for q and the first tile only, and the compiler never
 // sees q as a pending register load.
+// With NT tokens the NT q blocks of a sequence are contiguous ([B][NT][64][256]).
+template <int NT>
 __device__ __forceinline__ void issue_q(const AttnArgs& a, int b, char* qs, int w, int lane) {
-  const char* src = (const char*)a.q + (long long)b * (kHeads * kHeadDim * 2);
+  const char* src = (const char*)a.q + (long long)b * NT * (kHeads * kHeadDim * 2);
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const int blk = w * 8 + jj;  // 32 blocks of 1 KB
+    const int blk = w * 8 + jj;  // 32 NT blocks of 1 KB, 8 per wave
     __builtin_amdgcn_global_load_lds((const void*)(src + blk * 1024 + lane * 16), (MFA_LDS void*)(qs + blk * 1024),
                                      16, 0, 0);
   }
@@ -489,39 +497,56 @@ __device__ __forceinline__ void scores_fp8(const char* ks, int n, int g, const Q
 // are issued before the first block's softmax (which then runs on the vector
 // unit while the second block's products execute), and the second block's
 // softmax and V widening follow the issue of the first block's value product.
+// kEarlyV: read the second block's V with the first's (one wave per SIMD has
+// the registers; with two waves per SIMD it is read after the first softmax).
+template <bool kEarlyV>
 __device__ __forceinline__ void attend_tile_fp8(const char* ks, const char* vs, int nvalid, int n, int g,
                                                 const VReader<true>& vr, const Q8& q8, float score_mul, float& m_run,
                                                 float& l_run, f32x4 (&acc)[16]) {
   constexpr int kBlk = 32 * 256;  // bytes of a 32-row block of K or V
   score_mul *= q8.mul;
   f32x4 a0, a1, b0, b1;
-  i32x2 v8[16], w8[16];
+  i32x2 v8[16], w8[kEarlyV ? 16 : 1];
   bf16x8 vf[16];
   scores_fp8(ks, n, g, q8, a0, a1);
 #pragma unroll
   for (int db = 0; db < 16; ++db) v8[db] = vr.read8(vs, db);
   // rows past nvalid are masked, so the second block needs no branch
   scores_fp8(ks + kBlk, n, g, q8, b0, b1);
+  if constexpr (kEarlyV) {
 #pragma unroll
-  for (int db = 0; db < 16; ++db) w8[db] = vr.read8(vs + kBlk, db);
+    for (int db = 0; db < 16; ++db) w8[db] = vr.read8(vs + kBlk, db);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int db = 0; db < 16; ++db) vf[db] = widen8(v8[db]);
   softmax_pv(a0, a1, nvalid, g, score_mul, vf, m_run, l_run, acc);
+  if constexpr (!kEarlyV) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db) v8[db] = vr.read8(vs + kBlk, db);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int db = 0; db < 16; ++db) vf[db] = widen8(w8[db]);
+  for (int db = 0; db < 16; ++db) {
+    if constexpr (kEarlyV)
+      vf[db] = widen8(w8[db]);
+    else
+      vf[db] = widen8(v8[db]);
+  }
   softmax_pv(b0, b1, nvalid - 32, g, score_mul, vf, m_run, l_run, acc);
 }
 
-template <bool FP8, bool PAGED>
-__global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
-  using C = Cfg<FP8>;
-  // the 4-stage tile ring, then q (32 KB): 160 KB of LDS
-  __shared__ __attribute__((aligned(1024))) char ring[C::kStages * C::kTileBytes + kHeads * kHeadDim * 2];
+template <bool FP8, bool PAGED, int NT>
+__global__ __launch_bounds__(256 * NT, 1) void attn_mfma_kernel(AttnArgs a) {
+  using C = Cfg<FP8, NT>;
+  // the tile ring, then q (32 KB per token): 160 KB of LDS
+  __shared__ __attribute__((aligned(1024))) char ring[C::kLdsBytes];
   char* const qs = ring + C::kStages * C::kTileBytes;
   const int lane = threadIdx.x & 63;
-  const int w = uniform((int)(threadIdx.x >> 6));
+  const int wv = uniform((int)(threadIdx.x >> 6));
+  const int w = wv & 3;    // heads 16w..16w+15
+  const int tok = wv >> 2;  // new token (multi-token decode; 0 otherwise)
+  char* const qt = qs + tok * (kHeads * kHeadDim * 2);
   const int n = lane & 15;
   const int g = lane >> 4;
   const int wgi = piece_index(a.G);
@@ -531,12 +556,12 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
   Cursor<C::kRows, PAGED> cons = prod;
 
   // q of the first piece goes out ahead of the first tile DMAs.
-  issue_q(a, cons.b, qs, w, lane);
+  issue_q<NT>(a, cons.b, qs, wv, lane);
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < C::kStages - 1; ++s) {
     if (prod.valid()) {
-      issue_tile<FP8, PAGED>(a, prod, ring + s * C::kTileBytes, w, lane);
+      issue_tile<FP8, PAGED, NT>(a, prod, ring + s * C::kTileBytes, wv, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
@@ -552,7 +577,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();
   bf16x8 qf[8];
-  read_q<FP8>(qs, w, n, g, qf);
+  read_q<FP8>(qt, w, n, g, qf);
   Q8 q8;  // fp8 cache: q as hi/lo e4m3 pairs
   if constexpr (FP8) split_q8(qf, q8);
 
@@ -569,12 +594,15 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     if (fresh) {
       // Later pieces of the workgroup: a full drain for their q (rare). Every
       // wave finished reading the previous q right after it landed.
-      issue_q(a, cons.b, qs, w, lane);
+      issue_q<NT>(a, cons.b, qs, wv, lane);
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      read_q<FP8>(qs, w, n, g, qf);
+      read_q<FP8>(qt, w, n, g, qf);
       if constexpr (FP8) split_q8(qf, q8);
       m_run = -INFINITY;  // the first block rescales acc by exp2(-inf) = 0
+      // (a token that sees no row of the new piece never rescales: its sum
+      // must start from zero for the empty-token test at the piece's end)
+      if constexpr (NT > 1) l_run = 0.f;
       piece_lo = cons.gpos - cons.seq_start;
       fresh = false;
     }
@@ -585,26 +613,41 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
     drained = false;
     __builtin_amdgcn_s_barrier();
     if (prod.valid()) {
-      issue_tile<FP8, PAGED>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, w, lane);
+      issue_tile<FP8, PAGED, NT>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, wv, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
     char* stage = ring + (t % C::kStages) * C::kTileBytes;
     long long lo, hi;
     cons.tile(lo, hi);
-    const int nvalid = cons.valid_rows(lo, hi);
-    if constexpr (FP8)
-      attend_tile_fp8(stage, stage + C::kHalfBytes, nvalid, n, g, vr, q8, a.score_mul, m_run, l_run, acc);
-    else
-      attend_tile_bf16(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
+    int nvalid = cons.valid_rows(lo, hi);
+    if constexpr (NT > 1) {
+      // causal among the new tokens: token tok sees the rows before len - (NT - 1 - tok)
+      const long long lim = cons.len - (NT - 1 - tok);
+      nvalid = (int)((hi < lim ? hi : lim) - lo);
+    }
+    if (NT == 1 || nvalid > 0) {
+      if constexpr (FP8)
+        attend_tile_fp8<NT == 1>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, q8, a.score_mul, m_run, l_run,
+                                 acc);
+      else
+        attend_tile_bf16(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
+    }
 
     const long long pe = cons.part_end() - cons.seq_start;
     if (hi == pe) {
-      // finalize this piece of sequence cons.b
+      // finalize this piece of sequence cons.b (for token tok)
       const float lt = sum_over_rows(l_run);
-      const float inv = a.v_mul / lt;
-      const float lse2 = m_run + fast_log2(lt);
+      float inv = a.v_mul / lt;
+      float lse2 = m_run + fast_log2(lt);
+      if constexpr (NT > 1) {
+        if (!(lt > 0.f)) {  // the token saw no row of this piece: weight 0 in the merge
+          inv = 0.f;
+          lse2 = -INFINITY;
+        }
+      }
       const int h = 16 * w + n;
+      const long long bt = (long long)cons.b * NT + tok;  // output row of (sequence, token)
       const long long L = cons.seq_end - cons.seq_start;
       if (piece_lo == 0 && threadIdx.x == 0) {
         // this workgroup holds the sequence's first piece: tell the combine
@@ -613,20 +656,20 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_kernel(AttnArgs a) {
         *(i32x2*)(a.meta + 2 * cons.b) = i32x2{wgi + cons.b, np};
       }
       if (piece_lo == 0 && hi == L) {
-        bf16* orow = (bf16*)a.out + ((long long)cons.b * kHeads + h) * kHeadDim + 4 * g;
+        bf16* orow = (bf16*)a.out + (bt * kHeads + h) * kHeadDim + 4 * g;
 #pragma unroll
         for (int db = 0; db < 16; ++db) {
           const bf16x4 o = {(bf16)(acc[db][0] * inv), (bf16)(acc[db][1] * inv), (bf16)(acc[db][2] * inv),
                             (bf16)(acc[db][3] * inv)};
           *(bf16x4*)(orow + 16 * db) = o;
         }
-        if (a.lse != nullptr && g == 0) a.lse[(long long)cons.b * kHeads + h] = lse2 * kLn2;
+        if (a.lse != nullptr && g == 0) a.lse[bt * kHeads + h] = lse2 * kLn2;
       } else {
         // partial outputs in bf16 (half the bytes of the round trip through
         // memory; the merge weights stay fp32), in the register layout: one
         // 1 KB contiguous store per wave and channel-block pair (the combine
         // knows the map)
-        const long long slot = (long long)wgi + cons.b;
+        const long long slot = ((long long)wgi + cons.b) * NT + tok;
         bf16x8* prow = (bf16x8*)a.part_o + slot * (kHeads * kHeadDim / 8);
 #pragma unroll
         for (int dp = 0; dp < 8; ++dp) {
@@ -824,7 +867,11 @@ __global__ __launch_bounds__(256) void attn_combine_f32_kernel(AttnArgs a) {
 // 32dp + 4(lane/16) + {0..3} and the same + 16. Grid (B, 8): thread c of the
 // sequence merges chunk c of every partial.
 __global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
-  const int b = blockIdx.x;
+  // workgroup (bt, y): channel block y of output row bt = (sequence b, token tok)
+  const int bt = blockIdx.x;
+  const int nt = a.nt;  // 1, or 2 for multi-token decode
+  const int b = nt == 1 ? bt : bt >> 1;
+  const int tok = bt - b * nt;
   const int c = blockIdx.y * 256 + threadIdx.x;
   const int lane = c & 63, dp = (c >> 6) & 7, w = c >> 9;
   const int n = lane & 15, g = lane >> 4;
@@ -833,18 +880,20 @@ __global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
   // sequence is never written and not looked at)
   const long long L = load_scalar(a.seq_len, b);
   const i32x2 rec = load_scalar((const i32x2*)a.meta, b);
-  bf16* orow = (bf16*)a.out + ((long long)b * kHeads + h) * kHeadDim + 32 * dp + 4 * g;
+  bf16* orow = (bf16*)a.out + ((long long)bt * kHeads + h) * kHeadDim + 32 * dp + 4 * g;
   const bool lse_owner = a.lse != nullptr && dp == 0 && g == 0;
   // (np >= 0 always: the test only keeps the record load ahead of the branch)
   if ((L == 0) | (rec[1] < 0)) {
     *(bf16x4*)orow = bf16x4{};
     *(bf16x4*)(orow + 16) = bf16x4{};
-    if (lse_owner) a.lse[(long long)b * kHeads + h] = -INFINITY;
+    if (lse_owner) a.lse[(long long)bt * kHeads + h] = -INFINITY;
     return;
   }
   const int np = rec[1];
   if (np == 0) return;
-  const long long slot0 = rec[0];
+  // piece s of the sequence holds slot (slot0 + s) * nt + tok
+  const long long slot0 = (long long)rec[0] * nt + tok;
+  const long long lstride = (long long)nt * kHeads, pstride = (long long)nt * (kHeads * kHeadDim / 8);
   const float* lrow = a.part_lse + slot0 * kHeads + h;
   const bf16x8* prow = (const bf16x8*)a.part_o + slot0 * (kHeads * kHeadDim / 8) + c;
   constexpr int kBatch = 8;
@@ -856,32 +905,36 @@ __global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int s = s0 + k < np ? s0 + k : np - 1;
-      part[k] = prow[(long long)s * (kHeads * kHeadDim / 8)];
-      lw[k] = s0 + k < np ? lrow[(long long)s * kHeads] : -INFINITY;
+      part[k] = prow[s * pstride];
+      lw[k] = s0 + k < np ? lrow[s * lstride] : -INFINITY;
     }
     float mb = lw[0];
 #pragma unroll
     for (int k = 1; k < kBatch; ++k) mb = fmaxf(mb, lw[k]);
     const float m_new = fmaxf(m, mb);
-    const float sc = fast_exp2(m - m_new);  // 0 on the first batch
+    // (m_new = -inf only while every piece so far is empty for this token)
+    const bool none = m_new == -INFINITY;
+    const float sc = none ? 0.f : fast_exp2(m - m_new);  // 0 on the first batch
     wsum *= sc;
     o0 *= sc;
     o1 *= sc;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const float wt = fast_exp2(lw[k] - m_new);  // 0 for the padding entries
+      const float wt = none ? 0.f : fast_exp2(lw[k] - m_new);  // 0 for the padding entries
       wsum += wt;
       o0 += f32x4{(float)part[k][0], (float)part[k][1], (float)part[k][2], (float)part[k][3]} * wt;
       o1 += f32x4{(float)part[k][4], (float)part[k][5], (float)part[k][6], (float)part[k][7]} * wt;
     }
     m = m_new;
   }
-  const float inv = 1.f / wsum;
+  // wsum = 0: the token saw no row at all (multi-token decode on a short
+  // sequence): output 0 and lse -inf, as for an empty sequence
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   o0 *= inv;
   o1 *= inv;
   *(bf16x4*)orow = bf16x4{(bf16)o0[0], (bf16)o0[1], (bf16)o0[2], (bf16)o0[3]};
   *(bf16x4*)(orow + 16) = bf16x4{(bf16)o1[0], (bf16)o1[1], (bf16)o1[2], (bf16)o1[3]};
-  if (lse_owner) a.lse[(long long)b * kHeads + h] = (m + fast_log2(wsum)) * kLn2;
+  if (lse_owner) a.lse[(long long)bt * kHeads + h] = wsum > 0.f ? (m + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -895,18 +948,19 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
   a.out = p.out;
   a.lse = p.lse;
   a.part_o = p.ws;
-  a.part_lse = (float*)((char*)p.ws + attn_part_o_bytes(p.B, p.G));
-  a.meta = (int*)((char*)p.ws + attn_meta_offset(p.B, p.G));
+  a.part_lse = (float*)((char*)p.ws + attn_part_o_bytes(p.B, p.G, p.nt));
+  a.meta = (int*)((char*)p.ws + attn_meta_offset(p.B, p.G, p.nt));
   a.table = p.table;
   a.max_blocks = p.max_blocks;
   a.page_shift = p.page_shift;
+  a.nt = p.nt;
   a.B = p.B;
   a.G = p.G;
   a.score_mul = p.softmax_scale * p.k_scale * kLog2e;
   a.v_mul = p.v_scale;
   const dim3 block(256);
   const dim3 comb_f32(p.B, 16);
-  const dim3 comb_mfma(p.B, 8);
+  const dim3 comb_mfma(p.B * p.nt, 8);
   hipError_t e = hipSuccess;
   switch (p.kind) {
     case AttnKind::F32:
@@ -914,13 +968,19 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
       if (e == hipSuccess) e = launch(attn_combine_f32_kernel, comb_f32, block, stream, a);
       break;
     case AttnKind::BF16:
-      e = p.table ? launch(attn_mfma_kernel<false, true>, dim3(p.G), block, stream, a)
-                  : launch(attn_mfma_kernel<false, false>, dim3(p.G), block, stream, a);
+      if (p.nt == 2)  // (contiguous cache only)
+        e = launch(attn_mfma_kernel<false, false, 2>, dim3(p.G), dim3(512), stream, a);
+      else
+        e = p.table ? launch(attn_mfma_kernel<false, true, 1>, dim3(p.G), block, stream, a)
+                    : launch(attn_mfma_kernel<false, false, 1>, dim3(p.G), block, stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
-      e = p.table ? launch(attn_mfma_kernel<true, true>, dim3(p.G), block, stream, a)
-                  : launch(attn_mfma_kernel<true, false>, dim3(p.G), block, stream, a);
+      if (p.nt == 2)
+        e = launch(attn_mfma_kernel<true, false, 2>, dim3(p.G), dim3(512), stream, a);
+      else
+        e = p.table ? launch(attn_mfma_kernel<true, true, 1>, dim3(p.G), block, stream, a)
+                    : launch(attn_mfma_kernel<true, false, 1>, dim3(p.G), block, stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
   }

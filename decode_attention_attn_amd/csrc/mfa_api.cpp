@@ -224,13 +224,13 @@ size_t mfa_decode_attn_workspace_size(int B, int num_workgroups) {
 // Shared by the contiguous and the paged entry points (table == null: contiguous).
 static int decode_attn_impl(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
                             const int32_t* block_table, int max_blocks, int page_rows, const int32_t* seq_len,
-                            float softmax_scale, float k_scale, float v_scale, void* out, float* lse, void* ws,
-                            size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
+                            int n_tokens, float softmax_scale, float k_scale, float v_scale, void* out, float* lse,
+                            void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
                             void* stream) {
   const bool paged = block_table != nullptr;
   if (!q || !k_cache || !v_cache || (!paged && !seq_off) || !seq_len || !out || B < 1 || B > MFA_MAX_BATCH ||
       num_workgroups < 0 || num_workgroups > 65536 || !isfinite(softmax_scale) || !isfinite(k_scale) ||
-      !isfinite(v_scale))
+      !isfinite(v_scale) || n_tokens < 1 || n_tokens > 2)
     return MFA_ERR_INVALID_ARG;
   int page_shift = 0;
   if (paged) {
@@ -238,8 +238,9 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
       return MFA_ERR_INVALID_ARG;
     while ((1 << page_shift) < page_rows) ++page_shift;
   }
+  if (n_tokens > 1 && paged) return MFA_ERR_UNSUPPORTED;
   mfa::AttnKind kind;
-  if (q_dt == MFA_F32 && kv_dt == MFA_F32 && !paged)
+  if (q_dt == MFA_F32 && kv_dt == MFA_F32 && !paged && n_tokens == 1)
     kind = mfa::AttnKind::F32;
   else if (q_dt == MFA_BF16 && kv_dt == MFA_BF16)
     kind = mfa::AttnKind::BF16;
@@ -258,7 +259,7 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
     G = current_cu_count(&st);
     if (st != MFA_OK) return st;
   }
-  if (ws_bytes < mfa::attn_ws_bytes(B, G)) return MFA_ERR_WORKSPACE;
+  if (ws_bytes < mfa::attn_ws_bytes(B, G, n_tokens)) return MFA_ERR_WORKSPACE;
   mfa::AttnLaunch p;
   p.kind = kind;
   p.q = q;
@@ -277,6 +278,7 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
   p.table = block_table;
   p.max_blocks = paged ? max_blocks : 0;
   p.page_shift = page_shift;
+  p.nt = n_tokens;
   return hip_status(mfa::launch_decode_attn(p, (hipStream_t)stream));
 }
 
@@ -285,8 +287,30 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
                     void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
                     void* stream) {
   if (!seq_off) return MFA_ERR_INVALID_ARG;
-  return decode_attn_impl(q, k_cache, v_cache, seq_off, nullptr, 0, 0, seq_len, softmax_scale, k_scale, v_scale,
+  return decode_attn_impl(q, k_cache, v_cache, seq_off, nullptr, 0, 0, seq_len, 1, softmax_scale, k_scale, v_scale,
                           out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt, stream);
+}
+
+size_t mfa_decode_attn_mt_workspace_size(int B, int n_tokens, int num_workgroups) {
+  if (n_tokens < 1 || n_tokens > 2) return 0;
+  const size_t one = mfa_decode_attn_workspace_size(B, num_workgroups);
+  if (one == 0) return 0;
+  int G = num_workgroups;
+  if (G == 0) {
+    int st = MFA_OK;
+    G = current_cu_count(&st);
+    if (st != MFA_OK) return 0;
+  }
+  return mfa::attn_ws_bytes(B, G, n_tokens);
+}
+
+int mfa_decode_attn_mt(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                       const int32_t* seq_len, int n_tokens, float softmax_scale, float k_scale, float v_scale,
+                       void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt,
+                       mfa_dtype kv_dt, void* stream) {
+  if (!seq_off) return MFA_ERR_INVALID_ARG;
+  return decode_attn_impl(q, k_cache, v_cache, seq_off, nullptr, 0, 0, seq_len, n_tokens, softmax_scale, k_scale,
+                          v_scale, out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt, stream);
 }
 
 int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
@@ -294,8 +318,9 @@ int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_page
                           float v_scale, void* out, float* lse, void* ws, size_t ws_bytes, int B,
                           int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream) {
   if (!block_table) return MFA_ERR_INVALID_ARG;
-  return decode_attn_impl(q, k_pages, v_pages, nullptr, block_table, max_blocks, page_rows, seq_len, softmax_scale,
-                          k_scale, v_scale, out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt, stream);
+  return decode_attn_impl(q, k_pages, v_pages, nullptr, block_table, max_blocks, page_rows, seq_len, 1,
+                          softmax_scale, k_scale, v_scale, out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt,
+                          stream);
 }
 
 // ------------------------------------------------------------------ out-projection

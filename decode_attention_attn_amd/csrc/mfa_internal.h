@@ -45,14 +45,19 @@ struct AttnLaunch {
   const int32_t* table = nullptr;
   int max_blocks = 0;
   int page_shift = 0;
+  int nt = 1;  // query tokens per sequence (2: multi-token decode, contiguous cache)
 };
 
-// Workspace: partial outputs [G + B][64][256] (fp32-sized; bf16 partials use
-// half), partial lse [G + B][64] fp32, then per-sequence combine metadata
-// [B] x {first slot, piece count}.
-inline size_t attn_part_o_bytes(int B, int G) { return (size_t)(G + B) * 64 * 256 * sizeof(float); }
-inline size_t attn_meta_offset(int B, int G) { return attn_part_o_bytes(B, G) + (size_t)(G + B) * 64 * sizeof(float); }
-inline size_t attn_ws_bytes(int B, int G) { return attn_meta_offset(B, G) + (size_t)B * 2 * sizeof(int); }
+// Workspace: partial outputs [(G + B) nt][64][256] (fp32-sized; bf16 partials
+// use half), partial lse [(G + B) nt][64] fp32, then per-sequence combine
+// metadata [B] x {first slot, piece count}; nt = query tokens per sequence.
+inline size_t attn_part_o_bytes(int B, int G, int nt = 1) {
+  return (size_t)(G + B) * nt * 64 * 256 * sizeof(float);
+}
+inline size_t attn_meta_offset(int B, int G, int nt = 1) {
+  return attn_part_o_bytes(B, G, nt) + (size_t)(G + B) * nt * 64 * sizeof(float);
+}
+inline size_t attn_ws_bytes(int B, int G, int nt = 1) { return attn_meta_offset(B, G, nt) + (size_t)B * 2 * sizeof(int); }
 
 hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream);
 

@@ -221,6 +221,16 @@ def make_attn(w: Workload, lengths: Optional[np.ndarray] = None) -> dict:
                 seq_off=off, seq_len=lengths, kind_q=w.act, kind_kv=w.kv)
 
 
+def with_tokens(inp: dict, n_tokens: int) -> dict:
+    """Attention inputs with ``n_tokens`` query tokens per sequence (q
+    [B, n_tokens, 64, 256], drawn from the same stream as ``make_attn``'s q,
+    so n_tokens = 1 gives the same numbers); the cache is unchanged."""
+    w = inp["workload"]
+    B = len(inp["seq_len"])
+    q = store(normal(w.seed, ID_Q, (B, n_tokens, N_HEADS, HEAD_DIM)), w.act)
+    return dict(inp, q=q, n_tokens=n_tokens)
+
+
 def to_pages(inp: dict, page_rows: int, seed: int = 0, spare_pages: int = 3) -> dict:
     """Paged copy of attention inputs from ``make_attn``: the same keys and
     values, with each sequence's rows cut into blocks of ``page_rows`` and the

@@ -61,6 +61,10 @@ _lib.mfa_decode_attn_workspace_size.restype = _Z
 _lib.mfa_decode_attn_workspace_size.argtypes = [_I, _I]
 _lib.mfa_decode_attn.restype = _I
 _lib.mfa_decode_attn.argtypes = [_P, _P, _P, _P, _P, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
+_lib.mfa_decode_attn_mt_workspace_size.restype = _Z
+_lib.mfa_decode_attn_mt_workspace_size.argtypes = [_I, _I, _I]
+_lib.mfa_decode_attn_mt.restype = _I
+_lib.mfa_decode_attn_mt.argtypes = [_P, _P, _P, _P, _P, _I, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
 _lib.mfa_decode_attn_paged.restype = _I
 _lib.mfa_decode_attn_paged.argtypes = [_P, _P, _P, _P, _I, _I, _P, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
 _lib.mfa_oproj_workspace_size.restype = _Z
@@ -73,6 +77,7 @@ EXPORTED = [
     "mfa_qproj_workspace_size", "mfa_qproj",
     "mfa_kv_append_workspace_size", "mfa_kv_append", "mfa_kv_append_fp8",
     "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_paged",
+    "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
     "mfa_oproj_workspace_size", "mfa_oproj",
 ]
 
@@ -159,6 +164,17 @@ def mfa_decode_attn(q, k_cache, v_cache, seq_off, seq_len, softmax_scale, k_scal
     return _lib.mfa_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off), _ptr(seq_len),
                                 softmax_scale, k_scale, v_scale, _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), B,
                                 num_workgroups, q_dt, kv_dt, _stream(stream))
+
+
+def mfa_decode_attn_mt_workspace_size(B: int, n_tokens: int, num_workgroups: int = 0) -> int:
+    return _lib.mfa_decode_attn_mt_workspace_size(B, n_tokens, num_workgroups)
+
+
+def mfa_decode_attn_mt(q, k_cache, v_cache, seq_off, seq_len, n_tokens, softmax_scale, k_scale, v_scale, out, lse,
+                       ws, B, num_workgroups, q_dt, kv_dt, stream=None) -> int:
+    return _lib.mfa_decode_attn_mt(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off), _ptr(seq_len), n_tokens,
+                                   softmax_scale, k_scale, v_scale, _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), B,
+                                   num_workgroups, q_dt, kv_dt, _stream(stream))
 
 
 def mfa_decode_attn_paged(q, k_pages, v_pages, block_table, max_blocks, page_rows, seq_len, softmax_scale, k_scale,

@@ -69,7 +69,7 @@ def upload_attn(inp: dict, device="cuda") -> dict:
         table=to_device(inp["block_table"], "i32", device) if paged else None,
         max_blocks=int(inp["max_blocks"]) if paged else 0,
         page_rows=int(inp["page_rows"]) if paged else 0,
-        kind_q=inp["kind_q"], kind_kv=kk,
+        kind_q=inp["kind_q"], kind_kv=kk, nt=int(inp.get("n_tokens", 1)),
         k_scale=float(inp["k_scale"]) if inp["k_scale"] is not None else 1.0,
         v_scale=float(inp["v_scale"]) if inp["v_scale"] is not None else 1.0,
         B=len(inp["seq_len"]),
@@ -84,9 +84,11 @@ class AttnCall:
         self.G = num_workgroups
         B = dev["B"]
         device = dev["q"].device
-        self.out = torch.empty((B, 64, 256), dtype=_act_torch(dev["kind_q"]), device=device)
-        self.lse = torch.empty((B, 64), dtype=torch.float32, device=device) if want_lse else None
-        self.ws = _ws(mfa.mfa_decode_attn_workspace_size(B, num_workgroups), device)
+        nt = dev.get("nt", 1)
+        shape = (B, 64, 256) if nt == 1 else (B, nt, 64, 256)
+        self.out = torch.empty(shape, dtype=_act_torch(dev["kind_q"]), device=device)
+        self.lse = torch.empty(shape[:-1], dtype=torch.float32, device=device) if want_lse else None
+        self.ws = _ws(mfa.mfa_decode_attn_mt_workspace_size(B, nt, num_workgroups), device)
         self.stream = stream
 
     def __call__(self, k=None, v=None):
@@ -98,6 +100,11 @@ class AttnCall:
                                            SOFTMAX_SCALE, d["k_scale"], d["v_scale"], self.out, self.lse, self.ws,
                                            d["B"], self.G, _DT[d["kind_q"]], _DT[d["kind_kv"]], self.stream)
             mfa.check(st, "mfa_decode_attn_paged")
+        elif d.get("nt", 1) > 1:
+            st = mfa.mfa_decode_attn_mt(d["q"], k, v, d["off"], d["len"], d["nt"], SOFTMAX_SCALE, d["k_scale"],
+                                        d["v_scale"], self.out, self.lse, self.ws, d["B"], self.G,
+                                        _DT[d["kind_q"]], _DT[d["kind_kv"]], self.stream)
+            mfa.check(st, "mfa_decode_attn_mt")
         else:
             st = mfa.mfa_decode_attn(d["q"], k, v, d["off"], d["len"], SOFTMAX_SCALE, d["k_scale"], d["v_scale"],
                                      self.out, self.lse, self.ws, d["B"], self.G, _DT[d["kind_q"]],

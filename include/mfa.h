@@ -141,6 +141,26 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
                     void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups,
                     mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
 
+/* ------------------------------------------------------------------ attention, several new tokens
+ * Multi-token decode (speculative or multi-token-prediction verification;
+ * the pages' throughput figures exclude multi-token prediction, Step-3
+ * summary, "Key claims"): each sequence brings n_tokens new query tokens
+ * whose K/V rows are already the last n_tokens rows of its cache (seq_len
+ * counts them). Token t (0-based) of sequence b attends causally, over rows
+ * [seq_off[b], seq_off[b] + seq_len[b] - (n_tokens - 1 - t)); otherwise as
+ * mfa_decode_attn. q [B, n_tokens, 64, 256]; out [B, n_tokens, 64, 256];
+ * lse [B, n_tokens, 64] or NULL. A token that sees no row gets out = 0 and
+ * lse = -inf. n_tokens: 1 or 2 (else MFA_ERR_INVALID_ARG); 1 is exactly
+ * mfa_decode_attn. Supported (q_dt, kv_dt): (BF16, BF16), (BF16, FP8_E4M3)
+ * for n_tokens = 2. ws: at least mfa_decode_attn_mt_workspace_size(B,
+ * n_tokens, num_workgroups) bytes (0 for invalid arguments).
+ */
+size_t mfa_decode_attn_mt_workspace_size(int B, int n_tokens, int num_workgroups);
+int mfa_decode_attn_mt(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                       const int32_t* seq_len, int n_tokens, float softmax_scale, float k_scale,
+                       float v_scale, void* out, float* lse, void* ws, size_t ws_bytes, int B,
+                       int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
+
 /* ------------------------------------------------------------------ attention, paged cache
  * mfa_decode_attn over a paged cache: sequence b's rows live in fixed-size
  * pages of page_rows rows, its j-th block of page_rows keys (rows

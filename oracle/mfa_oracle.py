@@ -29,6 +29,9 @@ Readings where the pages are silent (each one is a choice this library makes):
     appended in this step included; no mask;
   * log-sum-exp uses the natural log; a sequence with no rows gives output 0
     and lse = -inf;
+  * with several new tokens per sequence (multi-token decode), their K/V
+    rows are the sequence's last rows and token t sees the rows before its
+    own successors (causal among the new tokens), none of the later ones;
   * a paged cache holds sequence b's keys j*R .. j*R + R - 1 (R rows per
     page) on page block_table[b][j]; it is the same sequence of keys, laid
     out in pages (the pages give no layout; paging is a serving choice);
@@ -217,6 +220,33 @@ def decode_attn(q, k_cache, v_cache, seq_off, seq_len, scale=SOFTMAX_SCALE,
         o, lse = attend_one(qb, kb, vb, scale)
         outs.append(o)
         lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+def decode_attn_mt(q, k_cache, v_cache, seq_off, seq_len, n_tokens, scale=SOFTMAX_SCALE,
+                   kind_q="f64", kind_kv="f64", k_scale=None, v_scale=None, batch_ids=None):
+    """Several new query tokens per sequence (q [B, n, H, D]), whose K/V rows are
+    the last n of the sequence's len_b rows: token t attends, causally, over
+    the first len_b - (n - 1 - t) rows (none if that is <= 0: output 0,
+    lse -inf). Returns (O [n_b, n, H, D], lse [n_b, n, H])."""
+    ids = range(len(seq_len)) if batch_ids is None else batch_ids
+
+    def up(a, kind, sc):
+        return np.asarray(a, dtype=np.float64) if kind == "f64" else to_f64(a, kind, sc)
+
+    outs, lses = [], []
+    for b in ids:
+        o0, L = int(seq_off[b]), int(seq_len[b])
+        kb = up(k_cache[o0:o0 + L], kind_kv, k_scale)
+        vb = up(v_cache[o0:o0 + L], kind_kv, v_scale)
+        ob, lb = [], []
+        for t in range(n_tokens):
+            m = max(0, L - (n_tokens - 1 - t))
+            o, lse = attend_one(up(q[b][t], kind_q, None), kb[:m], vb[:m], scale)
+            ob.append(o)
+            lb.append(lse)
+        outs.append(np.stack(ob))
+        lses.append(np.stack(lb))
     return np.stack(outs), np.stack(lses)
 
 

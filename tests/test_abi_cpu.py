@@ -96,6 +96,28 @@ def test_decode_attn_paged_rejects_bad_arguments():
     assert call(nbytes=mfa.mfa_decode_attn_workspace_size(4, 8) - 1) == mfa.MFA_ERR_WORKSPACE
 
 
+def test_decode_attn_mt_rejects_bad_arguments():
+    f = mfa.raw_function("mfa_decode_attn_mt")
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, off=FAKE, len=FAKE, n=2, out=FAKE, ws=FAKE, nbytes=1 << 40, B=4, G=8,
+                 qdt=mfa.MFA_BF16, kvdt=mfa.MFA_BF16)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["off"], a["len"], a["n"], 0.0625, 1.0, 1.0, a["out"], None, a["ws"],
+                 a["nbytes"], a["B"], a["G"], a["qdt"], a["kvdt"], None)
+
+    for n in (0, 3, -1):
+        assert call(n=n) == mfa.MFA_ERR_INVALID_ARG, n
+    assert call(off=None) == mfa.MFA_ERR_INVALID_ARG
+    assert call(qdt=mfa.MFA_F32, kvdt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
+    assert call(q=MIS) == mfa.MFA_ERR_ALIGNMENT
+    need1 = mfa.mfa_decode_attn_mt_workspace_size(4, 1, 8)
+    need2 = mfa.mfa_decode_attn_mt_workspace_size(4, 2, 8)
+    assert need1 == mfa.mfa_decode_attn_workspace_size(4, 8) and need2 > need1
+    assert mfa.mfa_decode_attn_mt_workspace_size(4, 3, 8) == 0
+    assert call(nbytes=need2 - 1) == mfa.MFA_ERR_WORKSPACE
+
+
 def test_projections_reject_bad_arguments():
     qp = mfa.raw_function("mfa_qproj")
     assert qp(None, FAKE, None, 1e-6, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_F32, None) == mfa.MFA_ERR_INVALID_ARG

@@ -1,0 +1,75 @@
+"""GPU parity of mfa_decode_attn_mt (two new query tokens per sequence,
+causal between them) against the float64 oracle (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+from parity import TOL, check, check_lse
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from decode_attention_attn_amd import inputs as gen  # noqa: E402
+from oracle import mfa_oracle as om  # noqa: E402
+
+WL = {"bf16": gen.WORKLOADS["attn_bf16_4k"], "fp8_e4m3": gen.WORKLOADS["attn_fp8kv_4k"]}
+# length 1: the first token sees no row (output 0, lse -inf); 0: empty sequence
+LENGTHS = np.array([2, 1, 31, 32, 33, 100, 257, 0, 700, 65], dtype=np.int32)
+
+
+def _run(inp, G=0):
+    from decode_attention_attn_amd import runner
+
+    dev = runner.upload_attn(inp)
+    out, lse = runner.AttnCall(dev, G)()
+    torch.cuda.synchronize()
+    return runner, runner.to_f64(out), runner.to_f64(lse)
+
+
+def _oracle(inp, ids=None):
+    return om.decode_attn_mt(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_off"], inp["seq_len"],
+                             inp["n_tokens"], kind_q=inp["kind_q"], kind_kv=inp["kind_kv"], k_scale=inp["k_scale"],
+                             v_scale=inp["v_scale"], batch_ids=ids)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("G", [1, 3, 0])
+def test_two_tokens_small(kind, G):
+    print(f"[case] two tokens {kind} G={G} lengths={LENGTHS.tolist()}", flush=True)
+    w = gen.scaled(WL[kind], batch=len(LENGTHS), ctx=0, seed=2)
+    inp = gen.with_tokens(gen.make_attn(w, lengths=LENGTHS), 2)
+    _, out, lse = _run(inp, G)
+    o_ref, l_ref = _oracle(inp)
+    t = TOL[kind]
+    check(f"two tokens out {kind} G={G}", out, o_ref, t["atol"], t["rel"])
+    check_lse(f"two tokens lse {kind} G={G}", lse, l_ref, t["lse"])
+
+
+@pytest.mark.parametrize("name,ids", [("attn_bf16_4k", [0, 15, 31]), ("attn_fp8kv_4k", [0, 31, 63])])
+def test_two_tokens_full_size(name, ids):
+    print(f"[case] two tokens {name} (full size, sampled sequences)", flush=True)
+    w = gen.WORKLOADS[name]
+    inp = gen.with_tokens(gen.make_attn(w), 2)
+    _, out, lse = _run(inp)
+    o_ref, l_ref = _oracle(inp, ids)
+    t = TOL[w.kv]
+    check(f"two tokens {name}", out[ids], o_ref, t["atol"], t["rel"])
+    check_lse(f"two tokens {name} lse", lse[ids], l_ref, t["lse"])
+
+
+def test_one_token_through_the_multi_token_entry_is_the_single_token_call():
+    print("[case] n_tokens = 1 via mfa_decode_attn_mt vs mfa_decode_attn", flush=True)
+    from decode_attention_attn_amd import mfa, runner
+
+    w = gen.scaled(WL["bf16"], batch=6, ctx=0, seed=3)
+    inp = gen.make_attn(w, lengths=np.array([3000, 17, 1500, 4096, 0, 129], dtype=np.int32))
+    o1, l1, dev = runner.decode_attn(inp)
+    B = dev["B"]
+    out = torch.empty_like(o1)
+    lse = torch.empty_like(l1)
+    ws = torch.empty(mfa.mfa_decode_attn_mt_workspace_size(B, 1, 0), dtype=torch.uint8, device="cuda")
+    mfa.check(mfa.mfa_decode_attn_mt(dev["q"], dev["k"], dev["v"], dev["off"], dev["len"], 1, 0.0625, 1.0, 1.0, out,
+                                     lse, ws, B, 0, mfa.MFA_BF16, mfa.MFA_BF16), "mfa_decode_attn_mt")
+    torch.cuda.synchronize()
+    assert torch.equal(out, o1) and torch.equal(lse, l1)

@@ -280,6 +280,32 @@ def test_any_partition_merges_back_by_lse():
     assert np.allclose(m + np.log(wts.sum(axis=0)), lse, atol=1e-12)
 
 
+def test_multi_token_decode_is_causal_by_brute_force():
+    # token t of n sees the first len - (n - 1 - t) rows: checked against the
+    # brute-force multi-head attention on each causal prefix, and a token with
+    # no row gives 0 / -inf
+    rng = np.random.default_rng(8)
+    lens = np.array([5, 1, 2, 0], dtype=np.int32)
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    q = rng.standard_normal((4, 2, 3, 8))
+    k = rng.standard_normal((8, 8))
+    v = rng.standard_normal((8, 8))
+    o, lse = om.decode_attn_mt(q, k, v, off, lens, 2, scale=0.5)
+    assert o.shape == (4, 2, 3, 8) and lse.shape == (4, 2, 3)
+    for b in range(4):
+        for t in range(2):
+            m = max(0, int(lens[b]) - (1 - t))
+            rows = list(range(int(off[b]), int(off[b]) + m))
+            if m == 0:
+                assert np.all(o[b, t] == 0) and np.all(lse[b, t] == -np.inf)
+                continue
+            bo, bl = brute.mha(q[b, t].tolist(), [k[rows].tolist()] * 3, [v[rows].tolist()] * 3, 0.5)
+            assert np.allclose(o[b, t], bo, atol=1e-12) and np.allclose(lse[b, t], bl, atol=1e-12)
+    # the last token sees the whole sequence: single-token decode of it
+    o1, l1 = om.decode_attn(q[:, 1], k, v, off, lens, scale=0.5)
+    assert np.array_equal(o[:, 1], o1) and np.array_equal(lse[:, 1], l1)
+
+
 def test_paged_rows_by_hand():
     # page 5 then page 2, 4 rows per page: keys 0..3 -> rows 20..23, keys 4..5 -> rows 8..9
     assert om.paged_rows([5, 2, 9], 6, 4).tolist() == [20, 21, 22, 23, 8, 9]
