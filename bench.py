@@ -12,8 +12,9 @@ already resident in HBM:
   * ``*_mtp2`` attention workloads: two new query tokens per sequence
     (causal between them), one ``mfa_decode_attn_mt`` call; tokens/s counts
     both;
-  * ``layer_bf16_8k`` / ``layer_bf16_fp8kv_8k`` / ``tiny_fp32``: the whole
-    decode layer (q path, K/V append, attention, out-projection).
+  * ``layer_bf16_8k`` / ``layer_bf16_fp8kv_8k`` / ``layer_fp8_8k`` (block-fp8
+    weights, e4m3 cache) / ``tiny_fp32``: the whole decode layer (q path, K/V
+    append, attention, out-projection).
 Prints one JSON line. ``value`` is KV-cache bytes read per second (GB/s) over
 the whole step; ``tokens_per_s`` is sequences decoded per second for this one
 layer. The K/V buffers rotate over several copies so that the 256 MB on-die
@@ -159,7 +160,9 @@ def bench_layer(name, steps, warmup, graph=True):
     B = w.batch
     esz = 4 if w.act == "f32" else 2
     kv = _kv_bytes(inp["seq_len"] + 1, w.kv)
-    weights = (2048 * 7168 + 16384 * 2048 + 2 * 256 * 7168 + 7168 * 16384) * esz
+    n_w = 2048 * 7168 + 16384 * 2048 + 2 * 256 * 7168 + 7168 * 16384
+    # block-fp8 weights: one byte per element plus one fp32 scale per 128 x 128 block
+    weights = n_w + 4 * (n_w // (128 * 128)) if w.weights == gen.FP8_BLOCK else n_w * esz
     return dict(workload=name, ms=ms, B=B, kv_bytes=kv, alg_bytes=kv + weights, lengths=inp["seq_len"] + 1,
                 inp=inp, w=w)
 
@@ -217,7 +220,7 @@ def main():
     ap.add_argument("--workload", default="attn_bf16_4k",
                     choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "attn_bf16_4k_paged",
                              "attn_fp8kv_4k_paged", "attn_bf16_4k_mtp2", "attn_fp8kv_4k_mtp2", "layer_bf16_8k",
-                             "layer_bf16_fp8kv_8k", "tiny_fp32"])
+                             "layer_bf16_fp8kv_8k", "layer_fp8_8k", "tiny_fp32"])
     ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -280,6 +283,7 @@ def main():
             "kv_heads": 1,
             "head_dim": 256,
             "kv_dtype": w.kv,
+            "weights": (w.weights or w.act) if w.kind == "layer" else None,
             "kv_buffer_sets": args.rotate if w.kind == "attn" else 1,
         },
         "tokens_per_s": round(res.get("tokens", w.batch) / (ms * 1e-3), 1),

@@ -144,6 +144,38 @@ int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, co
   return hip_status(e);
 }
 
+// Block-fp8 weights: the bf16 q path with e4m3 weight bytes and their
+// 128 x 128 block scales (the same plans, so the same workspace).
+int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps, const void* w_uq,
+                 const float* s_uq, void* q_out, void* ws, size_t ws_bytes, int B, void* stream) {
+  if (!x || !w_dq || !s_dq || !w_uq || !s_uq || !q_out || B < 1 || B > MFA_MAX_BATCH || !(eps >= 0.f) ||
+      !isfinite(eps))
+    return MFA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(q_out) || !aligned16(ws) ||
+      !aligned_n(s_dq, 4) || !aligned_n(s_uq, 4) || (gamma && !aligned_n(gamma, 4)))
+    return MFA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < qproj_ws(B, MFA_BF16, nullptr, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
+  mfa::GemmPlan plan, up;
+  int st = MFA_OK;
+  qproj_ws(B, MFA_BF16, &plan, &up, &st);
+  if (st != MFA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* part = (float*)ws;
+  size_t part_bytes = mfa::gemm_partial_bytes(plan);
+  if (up.splits > 1 && mfa::gemm_partial_bytes(up) > part_bytes) part_bytes = mfa::gemm_partial_bytes(up);
+  void* chat = (char*)ws + align256(part_bytes);
+  hipError_t e = mfa::launch_gemm(true, plan, x, w_dq, w_dq, part, mfa::GemmOut::Partial, s, s_dq, s_dq);
+  if (e != hipSuccess) return hip_status(e);
+  e = mfa::launch_rmsnorm_reduce(true, part, plan.splits, B, MFA_RANK, gamma, eps, chat, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (up.splits > 1) {
+    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s, s_uq, s_uq);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s));
+  }
+  return hip_status(mfa::launch_gemm(true, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s, s_uq, s_uq));
+}
+
 // ------------------------------------------------------------------ K/V append
 static size_t kv_ws(int B, mfa_dtype act_dt, mfa::GemmPlan* plan_out, int* status) {
   const bool bf = act_dt == MFA_BF16;
@@ -206,6 +238,35 @@ int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_c
   if (e != hipSuccess) return hip_status(e);
   e = mfa::launch_kv_scatter_fp8((const float*)ws, bf ? plan.splits : 1, B, k_cache, v_cache, seq_off, seq_len,
                                  inv_k, inv_v, s);
+  return hip_status(e);
+}
+
+int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const void* w_v, const float* s_v,
+                     void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len, mfa_dtype cache_dt,
+                     float k_scale, float v_scale, void* ws, size_t ws_bytes, int B, void* stream) {
+  if (!x || !w_k || !s_k || !w_v || !s_v || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 ||
+      B > MFA_MAX_BATCH)
+    return MFA_ERR_INVALID_ARG;
+  const bool fp8 = cache_dt == MFA_FP8_E4M3;
+  if (cache_dt != MFA_BF16 && !fp8) return MFA_ERR_UNSUPPORTED;
+  const float inv_k = 1.f / k_scale, inv_v = 1.f / v_scale;
+  if (fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale) ||
+              !isfinite(inv_k) || !isfinite(inv_v) || !(inv_k > 0.f) || !(inv_v > 0.f)))
+    return MFA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(ws) || !aligned_n(s_k, 4) || !aligned_n(s_v, 4) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
+    return MFA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < kv_ws(B, MFA_BF16, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
+  mfa::GemmPlan plan;
+  int st = MFA_OK;
+  kv_ws(B, MFA_BF16, &plan, &st);
+  if (st != MFA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = mfa::launch_gemm(true, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s, s_k, s_v);
+  if (e != hipSuccess) return hip_status(e);
+  e = fp8 ? mfa::launch_kv_scatter_fp8((const float*)ws, plan.splits, B, k_cache, v_cache, seq_off, seq_len, inv_k,
+                                       inv_v, s)
+          : mfa::launch_kv_scatter(true, (const float*)ws, plan.splits, B, k_cache, v_cache, seq_off, seq_len, s);
   return hip_status(e);
 }
 
@@ -357,6 +418,26 @@ int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_by
     return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s));
   }
   return hip_status(mfa::launch_gemm(bf, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s));
+}
+
+int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes, int B,
+                 void* stream) {
+  if (!attn || !w_o || !s_o || !y || B < 1 || B > MFA_MAX_BATCH) return MFA_ERR_INVALID_ARG;
+  if (!aligned16(attn) || !aligned16(w_o) || !aligned16(y) || !aligned16(ws) || !aligned_n(s_o, 4))
+    return MFA_ERR_ALIGNMENT;
+  const size_t need = oproj_ws(B, MFA_BF16, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need)) return MFA_ERR_WORKSPACE;
+  mfa::GemmPlan plan;
+  int st = MFA_OK;
+  oproj_ws(B, MFA_BF16, &plan, &st);
+  if (st != MFA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (plan.splits > 1) {
+    hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s, s_o, s_o);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s));
+  }
+  return hip_status(mfa::launch_gemm(true, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s, s_o, s_o));
 }
 
 }  // extern "C"

@@ -79,8 +79,9 @@ struct GemmPlan {
 // cus: compute units of the device (the split-K factor fills them once).
 GemmPlan plan_gemm(bool bf16, int M, int N, int K, int N0, int cus);
 size_t gemm_partial_bytes(const GemmPlan& p);
+// S0 / S1 non-null: W0 / W1 are block-fp8 (e4m3 bytes, fp32 scales per 128 x 128 block, [rows/128][K/128])
 hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
-                       GemmOut mode, hipStream_t stream);
+                       GemmOut mode, hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr);
 
 // c_hat[M, N] = rmsnorm(sum_s part[s]) * gamma, in the activation dtype.
 hipError_t launch_rmsnorm_reduce(bool bf16, const float* part, int S, int M, int N, const float* gamma,

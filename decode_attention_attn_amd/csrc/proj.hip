@@ -29,12 +29,15 @@ constexpr int kGK = 64;     // K per stage
 // tile (8 waves, 256 columns) reads each activation chunk once per 256
 // weight rows instead of 128, which halves the activation share of the bytes
 // a workgroup streams; it is used for the wide products (the out-projection).
-template <int NW>
+// W8: block-fp8 weights (e4m3 bytes, 64-byte rows per chunk), widened to bf16
+// in registers; the ring then holds 4 stages of 24 KB or 32 KB.
+template <int NW, bool W8 = false>
 struct GTile {
   static constexpr int kN = NW;                      // output columns per workgroup
   static constexpr int kWaves = NW / 32;             // 4 or 8
-  static constexpr int kStages = NW == 128 ? 4 : 3;  // LDS ring (64 KB or 48 KB stages)
-  static constexpr int kWBytes = NW * kGK * 2;       // weight tile
+  static constexpr int kStages = (NW == 128 || W8) ? 4 : 3;
+  static constexpr int kWRow = W8 ? kGK : kGK * 2;   // bytes of one weight row per chunk
+  static constexpr int kWBytes = NW * kWRow;         // weight tile
   static constexpr int kXBytes = kGM * kGK * 2;      // activation tile (16 KB)
   static constexpr int kStageBytes = kWBytes + kXBytes;
   static constexpr int kDmaPerWave = (kStageBytes / 1024) / kWaves;  // 8 or 6
@@ -43,11 +46,17 @@ struct GTile {
 
 struct GemmArgs {
   const bf16* X;
-  const bf16* W0;
+  const bf16* W0;  // (e4m3 bytes for block-fp8 weights)
   const bf16* W1;
   void* Y;
   int M, N, K, N0, S;
+  const float* S0;  // block-fp8: [rows / 128][K / 128] scales of W0 / W1
+  const float* S1;
 };
+
+// 16-byte chunk swizzle for the 64-byte rows of a block-fp8 weight chunk:
+// the 16 rows one MFMA fragment reads at a time land on distinct banks.
+__device__ __forceinline__ int gswz8(int r) { return (r >> 2) & 3; }
 
 // 16-byte chunk swizzle for 128-byte rows: conflict-free ds_read_b128 of 16
 // consecutive rows at one logical chunk for 32- and 64-bank LDS.
@@ -56,9 +65,9 @@ __device__ __forceinline__ int gswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // One K chunk of the weight tile (T::kN rows) and the activation tile (128
 // rows) into a ring stage: 1 KB blocks of 8 rows x 128 B, dealt evenly to
 // the waves (weight blocks first).
-template <int NW>
+template <int NW, bool W8>
 __device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, int kc, char* stage, int w, int lane) {
-  using T = GTile<NW>;
+  using T = GTile<NW, W8>;
   const int r_in = lane >> 3;  // 8 rows of 128 B per 1 KB block
   const int pc = lane & 7;
   const int k0 = kc * kGK;
@@ -66,7 +75,16 @@ __device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, in
 #pragma unroll
   for (int jj = 0; jj < T::kDmaPerWave; ++jj) {
     const int blk = T::kDmaPerWave * w + jj;
-    if (blk < kWBlocks) {
+    if (W8 && blk < kWBlocks) {
+      // 16 rows of 64 B per 1 KB block
+      const int r = 16 * blk + (lane >> 2);
+      const int c = (lane & 3) ^ gswz8(r);
+      const int n = n0 + r;
+      const unsigned char* wrow = n < a.N0 ? (const unsigned char*)a.W0 + (long long)n * a.K
+                                            : (const unsigned char*)a.W1 + (long long)(n - a.N0) * a.K;
+      __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 16), (MFA_LDS void*)(stage + blk * 1024), 16,
+                                       0, 0);
+    } else if (blk < kWBlocks) {
       const int r = 8 * blk + r_in;
       const int c = pc ^ gswz(r);
       const int n = n0 + r;
@@ -85,9 +103,9 @@ __device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, in
   }
 }
 
-template <GemmOut MODE, int NW>
+template <GemmOut MODE, int NW, bool W8 = false>
 __global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
-  using T = GTile<NW>;
+  using T = GTile<NW, W8>;
   constexpr int kGStages = T::kStages;
   constexpr int kGStageBytes = T::kStageBytes;
   constexpr int kGSteadyVm = T::kSteadyVm;
@@ -112,11 +130,25 @@ __global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Block-fp8 weights: this wave's 128 weight rows form one row of scale
+  // blocks, so a 64-wide K chunk has one scale (blocks are 128 x 128). The
+  // row index is wave-uniform, so the scale reads are scalar loads, which do
+  // not touch the vector-memory counter the DMA ring waits on; each chunk's
+  // scale is read one chunk ahead.
+  const float* srow = nullptr;
+  float sc_next = 0.f;
+  if constexpr (W8) {
+    const int nrow = n0 + __builtin_amdgcn_readfirstlane(wn);
+    srow = nrow < a.N0 ? a.S0 + (long long)(nrow >> 7) * (a.K >> 7)
+                       : a.S1 + (long long)((nrow - a.N0) >> 7) * (a.K >> 7);
+    if (nloc > 0) sc_next = load_scalar(srow, c_begin >> 1);
+  }
+
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < kGStages - 1; ++s)
     if (issued < nloc) {
-      gemm_issue<NW>(a, n0, m0, c_begin + issued, ring + s * kGStageBytes, wave, lane);
+      gemm_issue<NW, W8>(a, n0, m0, c_begin + issued, ring + s * kGStageBytes, wave, lane);
       ++issued;
     }
 
@@ -127,11 +159,48 @@ __global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (issued < nloc) {
-      gemm_issue<NW>(a, n0, m0, c_begin + issued, ring + ((t + kGStages - 1) % kGStages) * kGStageBytes, wave, lane);
+      gemm_issue<NW, W8>(a, n0, m0, c_begin + issued, ring + ((t + kGStages - 1) % kGStages) * kGStageBytes, wave,
+                         lane);
       ++issued;
     }
-    const char* ws = ring + (t % kGStages) * kGStageBytes + wn * 128;
     const char* xs = ring + (t % kGStages) * kGStageBytes + T::kWBytes;
+    if constexpr (W8) {
+      // The chunk's product is formed from the exact bf16 widening of the
+      // bytes, then scaled into the accumulator in fp32.
+      const float sc = sc_next;
+      sc_next = load_scalar(srow, (c_begin + (t + 1 < nloc ? t + 1 : t)) >> 1);
+      const char* ws8 = ring + (t % kGStages) * kGStageBytes + wn * T::kWRow;
+      f32x4 tmp[2][8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = 4 * j + g;  // 8-element chunk of the 64: bytes 8c..8c+7 of the row
+        bf16x8 wa[8], xb[2];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int r = 16 * nb + i16;
+          const u32x2 raw = *(const MFA_LDS u32x2*)(ws8 + r * 64 + ((((c >> 1) ^ gswz8(r))) << 4) + ((c & 1) << 3));
+          fp8x4_to_bf16(raw[0], wa[nb], 0);
+          fp8x4_to_bf16(raw[1], wa[nb], 4);
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int r = 16 * (2 * w + mi) + i16;
+          xb[mi] = *(const MFA_LDS bf16x8*)(xs + r * 128 + ((c ^ gswz(r)) << 4));
+        }
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+            tmp[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                wa[nb], xb[mi], j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : tmp[mi][nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[mi][nb] += tmp[mi][nb] * sc;
+      continue;
+    }
+    const char* ws = ring + (t % kGStages) * kGStageBytes + wn * 128;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = 4 * j + g;
@@ -348,13 +417,21 @@ GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) {
 size_t gemm_partial_bytes(const GemmPlan& p) { return (size_t)p.splits * p.M * p.N * sizeof(float); }
 
 hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
-                       GemmOut mode, hipStream_t stream) {
+                       GemmOut mode, hipStream_t stream, const float* S0, const float* S1) {
   if (!bf16_path) {
     return launch(gemm_f32_kernel, dim3((p.N + 3) / 4), dim3(256), stream, (const float*)X, (const float*)W0,
                        (const float*)W1, (float*)Y, p.M, p.N, p.K, p.N0);
   }
-  GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits};
+  GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits, S0, S1};
   const dim3 grid(p.N / p.tile_n, p.splits, p.mchunks);
+  if (S0 != nullptr) {  // block-fp8 weights
+    if (p.tile_n == 256)
+      return mode == GemmOut::Partial
+                 ? launch(gemm_bf16_kernel<GemmOut::Partial, 256, true>, grid, dim3(512), stream, a)
+                 : launch(gemm_bf16_kernel<GemmOut::Direct, 256, true>, grid, dim3(512), stream, a);
+    return mode == GemmOut::Partial ? launch(gemm_bf16_kernel<GemmOut::Partial, 128, true>, grid, dim3(256), stream, a)
+                                    : launch(gemm_bf16_kernel<GemmOut::Direct, 128, true>, grid, dim3(256), stream, a);
+  }
   if (p.tile_n == 256) {
     if (mode == GemmOut::Partial) return launch(gemm_bf16_kernel<GemmOut::Partial, 256>, grid, dim3(512), stream, a);
     return launch(gemm_bf16_kernel<GemmOut::Direct, 256>, grid, dim3(512), stream, a);

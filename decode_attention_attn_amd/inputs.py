@@ -40,6 +40,7 @@ QDIM = N_HEADS * HEAD_DIM  # 16384
 ID_X, ID_WDQ, ID_WUQ, ID_WK, ID_WV, ID_WO, ID_Q, ID_K, ID_V, ID_LEN, ID_PAGES = range(11)
 
 F32, BF16, FP8 = "f32", "bf16", "fp8_e4m3"
+FP8_BLOCK = "fp8_block"  # weights: e4m3 bytes with one fp32 scale per 128 x 128 block
 
 E4M3_MAX = 448.0
 
@@ -105,6 +106,19 @@ def quantize_e4m3fn(x: np.ndarray):
     return codes, scale
 
 
+def quantize_blocks_e4m3fn(w: np.ndarray, block: int = 128):
+    """Block-fp8 storage of a weight [out, in]: one float32 scale per
+    block x block tile (its amax / 448, 1 for an all-zero tile) and the e4m3
+    bytes of w / scale. Returns (codes uint8 [out, in], scales float32
+    [out / block, in / block])."""
+    w = np.asarray(w, dtype=np.float32)
+    o, i = w.shape
+    t = np.abs(w).reshape(o // block, block, i // block, block).max(axis=(1, 3))
+    scales = np.where(t > 0, t / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    full = np.repeat(np.repeat(scales.astype(np.float64), block, axis=0), block, axis=1)
+    return encode_e4m3fn(w.astype(np.float64) / full), scales
+
+
 def store(x: np.ndarray, kind: str):
     """float32 draws -> storage array for ``kind`` (fp32 copy or bf16 bits)."""
     if kind == F32:
@@ -159,6 +173,7 @@ class Workload:
     ragged: Optional[tuple] = None  # (lo, hi) closed interval of lengths
     seed: int = 0
     description: str = ""
+    weights: str = ""  # "" = stored like the activations; FP8_BLOCK = e4m3 with 128 x 128 block scales
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -177,6 +192,10 @@ WORKLOADS: Dict[str, Workload] = {
     "layer_bf16_8k": Workload(
         "layer_bf16_8k", "layer", 128, 8192, BF16, BF16,
         description="bf16 decode layer, batch 128, 8192 cached rows + 1 appended (8193 attended)"),
+    "layer_fp8_8k": Workload(
+        "layer_fp8_8k", "layer", 128, 8192, BF16, FP8, weights=FP8_BLOCK,
+        description="the FP8 decode layer: block-fp8 weights (e4m3, 128 x 128 block scales), bf16 activations, "
+                    "e4m3fn K/V cache, batch 128, 8192 cached rows + 1 appended"),
     "layer_bf16_fp8kv_8k": Workload(
         "layer_bf16_fp8kv_8k", "layer", 128, 8192, BF16, FP8,
         description="bf16 decode layer over an e4m3fn K/V cache (per-tensor scales, new rows quantized on "
@@ -275,11 +294,16 @@ def make_layer(w: Workload) -> dict:
     off = packed_offsets(cap)
     total_rows = int(cap.sum())
     x = store(normal(w.seed, ID_X, (B, HIDDEN)), w.act)
-    w_dq = store(weight(w.seed, ID_WDQ, RANK, HIDDEN), w.act)
-    w_uq = store(weight(w.seed, ID_WUQ, QDIM, RANK), w.act)
-    w_k = store(weight(w.seed, ID_WK, HEAD_DIM, HIDDEN), w.act)
-    w_v = store(weight(w.seed, ID_WV, HEAD_DIM, HIDDEN), w.act)
-    w_o = store(weight(w.seed, ID_WO, HIDDEN, QDIM), w.act)
+    draws = dict(w_dq=weight(w.seed, ID_WDQ, RANK, HIDDEN), w_uq=weight(w.seed, ID_WUQ, QDIM, RANK),
+                 w_k=weight(w.seed, ID_WK, HEAD_DIM, HIDDEN), w_v=weight(w.seed, ID_WV, HEAD_DIM, HIDDEN),
+                 w_o=weight(w.seed, ID_WO, HIDDEN, QDIM))
+    wts = {}
+    for name, d in draws.items():
+        if w.weights == FP8_BLOCK:
+            wts[name], wts[name + "_scale"] = quantize_blocks_e4m3fn(d)
+        else:
+            wts[name] = store(d, w.act)
+    del draws
     caches, scales = [], []
     for tid in (ID_K, ID_V):
         draws = normal(w.seed, tid, (B * ctx, HEAD_DIM)).reshape(B, ctx, HEAD_DIM)
@@ -296,7 +320,7 @@ def make_layer(w: Workload) -> dict:
             full[:, :ctx, :] = draws
             caches.append(store(full.reshape(total_rows, HEAD_DIM), w.kv))
             scales.append(None)
-    return dict(workload=w, x=x, w_dq=w_dq, w_uq=w_uq, w_k=w_k, w_v=w_v, w_o=w_o,
+    return dict(workload=w, x=x, **wts,
                 k_cache=caches[0], v_cache=caches[1], k_scale=scales[0], v_scale=scales[1], seq_off=off,
                 seq_len=np.full(B, ctx, dtype=np.int32), capacity=cap,
-                kind_act=w.act, kind_kv=w.kv, eps=1e-6)
+                kind_act=w.act, kind_kv=w.kv, kind_w=w.weights or w.act, eps=1e-6)

@@ -67,6 +67,12 @@ _lib.mfa_decode_attn_mt.restype = _I
 _lib.mfa_decode_attn_mt.argtypes = [_P, _P, _P, _P, _P, _I, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
 _lib.mfa_decode_attn_paged.restype = _I
 _lib.mfa_decode_attn_paged.argtypes = [_P, _P, _P, _P, _I, _I, _P, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
+_lib.mfa_qproj_w8.restype = _I
+_lib.mfa_qproj_w8.argtypes = [_P, _P, _P, _P, _F, _P, _P, _P, _P, _Z, _I, _P]
+_lib.mfa_kv_append_w8.restype = _I
+_lib.mfa_kv_append_w8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _F, _P, _Z, _I, _P]
+_lib.mfa_oproj_w8.restype = _I
+_lib.mfa_oproj_w8.argtypes = [_P, _P, _P, _P, _P, _Z, _I, _P]
 _lib.mfa_oproj_workspace_size.restype = _Z
 _lib.mfa_oproj_workspace_size.argtypes = [_I, _I]
 _lib.mfa_oproj.restype = _I
@@ -79,6 +85,7 @@ EXPORTED = [
     "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_paged",
     "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
     "mfa_oproj_workspace_size", "mfa_oproj",
+    "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8",
 ]
 
 
@@ -196,3 +203,19 @@ def mfa_oproj(attn, w_o, y, ws, B, dt, stream=None) -> int:
 def raw_function(name: str):
     """The ctypes function object of an exported symbol (for ABI tests)."""
     return getattr(_lib, name)
+
+
+def mfa_qproj_w8(x, w_dq, s_dq, gamma, eps, w_uq, s_uq, q_out, ws, B, stream=None) -> int:
+    return _lib.mfa_qproj_w8(_ptr(x), _ptr(w_dq), _ptr(s_dq), _ptr(gamma), eps, _ptr(w_uq), _ptr(s_uq), _ptr(q_out),
+                             _ptr(ws), _nbytes(ws), B, _stream(stream))
+
+
+def mfa_kv_append_w8(x, w_k, s_k, w_v, s_v, k_cache, v_cache, seq_off, seq_len, cache_dt, k_scale, v_scale, ws, B,
+                     stream=None) -> int:
+    return _lib.mfa_kv_append_w8(_ptr(x), _ptr(w_k), _ptr(s_k), _ptr(w_v), _ptr(s_v), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(seq_off), _ptr(seq_len), cache_dt, float(k_scale), float(v_scale), _ptr(ws),
+                                 _nbytes(ws), B, _stream(stream))
+
+
+def mfa_oproj_w8(attn, w_o, s_o, y, ws, B, stream=None) -> int:
+    return _lib.mfa_oproj_w8(_ptr(attn), _ptr(w_o), _ptr(s_o), _ptr(y), _ptr(ws), _nbytes(ws), B, _stream(stream))

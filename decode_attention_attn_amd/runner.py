@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import mfa
-from .inputs import BF16, F32, FP8
+from .inputs import BF16, F32, FP8, FP8_BLOCK
 
 SOFTMAX_SCALE = 1.0 / math.sqrt(256.0)
 
@@ -123,9 +123,15 @@ def decode_attn(inp: dict, num_workgroups: int = 0, device="cuda"):
 
 
 def upload_layer(inp: dict, device="cuda") -> dict:
-    ka, kk = inp["kind_act"], inp["kind_kv"]
-    d = {n: to_device(inp[n], ka, device) for n in ("x", "w_dq", "w_uq", "w_k", "w_v", "w_o")}
-    d.update(k=to_device(inp["k_cache"], kk, device), v=to_device(inp["v_cache"], kk, device),
+    ka, kk, kw = inp["kind_act"], inp["kind_kv"], inp.get("kind_w", inp["kind_act"])
+    d = {"x": to_device(inp["x"], ka, device)}
+    for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o"):
+        if kw == FP8_BLOCK:
+            d[n] = to_device(inp[n], FP8, device)
+            d[n + "_scale"] = to_device(inp[n + "_scale"], F32, device)
+        else:
+            d[n] = to_device(inp[n], kw, device)
+    d.update(kind_w=kw, k=to_device(inp["k_cache"], kk, device), v=to_device(inp["v_cache"], kk, device),
              off=to_device(inp["seq_off"], "i64", device), len=to_device(inp["seq_len"], "i32", device),
              kind_act=ka, kind_kv=kk, B=len(inp["seq_len"]), eps=float(inp.get("eps", 1e-6)),
              k_scale=float(inp["k_scale"]) if inp.get("k_scale") is not None else 1.0,
@@ -143,6 +149,8 @@ class LayerCall:
         at = _act_torch(dev["kind_act"])
         dt = _DT[dev["kind_act"]]
         self.dt = dt
+        if dev["kind_w"] == FP8_BLOCK and dev["kind_act"] != BF16:
+            raise ValueError("block-fp8 weights take bf16 activations")
         self.G = num_workgroups
         self.stream = stream
         self.q = torch.empty((B, 64, 256), dtype=at, device=device)
@@ -158,6 +166,8 @@ class LayerCall:
     def __call__(self):
         d, dt, s = self.dev, self.dt, self.stream
         B = d["B"]
+        if d["kind_w"] == FP8_BLOCK:
+            return self._call_w8()
         mfa.check(mfa.mfa_qproj(d["x"], d["w_dq"], None, d["eps"], d["w_uq"], self.q, self.ws_q, B, dt, s),
                   "mfa_qproj")
         if d["kind_kv"] == FP8:
@@ -173,4 +183,22 @@ class LayerCall:
                                       _DT[d["kind_kv"]], s),
                   "mfa_decode_attn")
         mfa.check(mfa.mfa_oproj(self.o, d["w_o"], self.y, self.ws_o, B, dt, s), "mfa_oproj")
+        return self
+
+    def _call_w8(self):
+        # block-fp8 weights: the same four steps through the _w8 entry points
+        # (bf16 activations; the cache is bf16 or e4m3)
+        d, dt, s = self.dev, self.dt, self.stream
+        B = d["B"]
+        mfa.check(mfa.mfa_qproj_w8(d["x"], d["w_dq"], d["w_dq_scale"], None, d["eps"], d["w_uq"], d["w_uq_scale"],
+                                   self.q, self.ws_q, B, s), "mfa_qproj_w8")
+        mfa.check(mfa.mfa_kv_append_w8(d["x"], d["w_k"], d["w_k_scale"], d["w_v"], d["w_v_scale"], d["k"], d["v"],
+                                       d["off"], d["len"], _DT[d["kind_kv"]], d["k_scale"], d["v_scale"],
+                                       self.ws_kv, B, s), "mfa_kv_append_w8")
+        torch.add(d["len"], 1, out=self.len_after)
+        mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
+                                      d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
+                                      _DT[d["kind_kv"]], s),
+                  "mfa_decode_attn")
+        mfa.check(mfa.mfa_oproj_w8(self.o, d["w_o"], d["w_o_scale"], self.y, self.ws_o, B, s), "mfa_oproj_w8")
         return self

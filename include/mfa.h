@@ -191,6 +191,30 @@ size_t mfa_oproj_workspace_size(int B, mfa_dtype dt);
 int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_bytes, int B,
               mfa_dtype dt, void* stream);
 
+/* ------------------------------------------------------------------ block-fp8 weights
+ * The projections with block-fp8 weights (the model's checkpoints come in
+ * bf16 and in block-fp8, and it runs in FP8: step3-fp8 model card, precision
+ * notes; Step-3 summary, "Key claims"). A weight W [out, in] is given as e4m3
+ * bytes W8 [out, in] (OCP E4M3 "fn") and fp32 scales S [out/128][in/128], one
+ * per 128 x 128 block, row-major: W[n][k] = W8[n][k] * S[n/128][k/128]. Each
+ * call computes what its bf16 counterpart computes with that W (bf16
+ * activations and outputs, fp32 accumulation; the bytes are widened exactly
+ * and each 64-wide slice of a block is scaled in fp32). Workspace sizes are
+ * those of the bf16 calls (mfa_qproj_workspace_size(B, MFA_BF16), ...).
+ * mfa_kv_append_w8 writes a bf16 cache (cache_dt = MFA_BF16, scales unused)
+ * or an e4m3 cache as mfa_kv_append_fp8 does (cache_dt = MFA_FP8_E4M3).
+ * Scale arrays: device fp32, 4-byte aligned.
+ */
+int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps,
+                 const void* w_uq, const float* s_uq, void* q_out, void* ws, size_t ws_bytes, int B,
+                 void* stream);
+int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const void* w_v, const float* s_v,
+                     void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len,
+                     mfa_dtype cache_dt, float k_scale, float v_scale, void* ws, size_t ws_bytes, int B,
+                     void* stream);
+int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes,
+                 int B, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

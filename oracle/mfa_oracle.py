@@ -35,6 +35,8 @@ Readings where the pages are silent (each one is a choice this library makes):
   * a paged cache holds sequence b's keys j*R .. j*R + R - 1 (R rows per
     page) on page block_table[b][j]; it is the same sequence of keys, laid
     out in pages (the pages give no layout; paging is a serving choice);
+  * block-fp8 weights (the model card's checkpoint format) are e4m3 bytes
+    with one float32 scale per 128 x 128 block: W = bytes * scale, exactly;
   * an fp8 cache is OCP E4M3 ("fn") bytes with one float32 scale per tensor
     (the model runs in FP8, attention included: Step-3 summary, "Key
     claims"); a new row is stored as e4m3(x / scale), rounded to nearest with
@@ -125,13 +127,23 @@ def quantize_e4m3fn(x, scale) -> np.ndarray:
     return encode_e4m3fn(np.asarray(x, dtype=np.float64) / np.float64(np.float32(scale)))
 
 
+def dequantize_blocks_e4m3fn(codes, scales, block: int = 128) -> np.ndarray:
+    """Block-fp8 weight -> float64: W[n][k] = e4m3(codes[n][k]) * scales[n // block][k // block]
+    (each product is exact in float64)."""
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    full = np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+    return _E4M3[np.asarray(codes, dtype=np.uint8)] * full
+
+
 def decode_e4m3fn(codes: np.ndarray, scale) -> np.ndarray:
     """fp8 bytes with a per-tensor float32 scale -> float64 (the product is exact)."""
     return _E4M3[np.asarray(codes, dtype=np.uint8)] * np.float64(np.float32(scale))
 
 
 def to_f64(arr: np.ndarray, kind: str, scale=None) -> np.ndarray:
-    """Upcast a stored tensor ("f32", "bf16" bit patterns or "fp8_e4m3" bytes) to float64."""
+    """Upcast a stored tensor ("f64", "f32", "bf16" bit patterns or "fp8_e4m3" bytes) to float64."""
+    if kind == "f64":
+        return np.asarray(arr, dtype=np.float64)
     if kind == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if kind == "bf16":
@@ -298,7 +310,11 @@ def decode_layer(inp: dict, batch_ids=None, scale=SOFTMAX_SCALE):
     ka, kk = inp["kind_act"], inp["kind_kv"]
     ids = list(range(len(inp["seq_len"]))) if batch_ids is None else list(batch_ids)
     x = to_f64(inp["x"], ka)[ids]
-    w = {n: to_f64(inp[n], ka) for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o")}
+    kw = inp.get("kind_w", ka)
+    if kw == "fp8_block":
+        w = {n: dequantize_blocks_e4m3fn(inp[n], inp[n + "_scale"]) for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o")}
+    else:
+        w = {n: to_f64(inp[n], kw) for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o")}
     c, c_hat, q = q_path(x, w["w_dq"], w["w_uq"], inp.get("eps", 1e-6), inp.get("gamma"))
     k_new, v_new = kv_project(x, w["w_k"], w["w_v"])
     ks, vs = inp.get("k_scale"), inp.get("v_scale")

@@ -160,6 +160,50 @@ def test_projections_reject_bad_arguments():
         assert op(FAKE, FAKE, FAKE, FAKE, need - 1, 128, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
 
 
+def test_block_fp8_projections_reject_bad_arguments():
+    qp = mfa.raw_function("mfa_qproj_w8")
+
+    def qcall(**kw):
+        a = dict(dict(x=FAKE, wdq=FAKE, sdq=FAKE, g=None, eps=1e-6, wuq=FAKE, suq=FAKE, q=FAKE, ws=FAKE,
+                      nbytes=1 << 30, B=2), **kw)
+        return qp(a["x"], a["wdq"], a["sdq"], a["g"], a["eps"], a["wuq"], a["suq"], a["q"], a["ws"], a["nbytes"],
+                  a["B"], None)
+
+    for bad in (dict(sdq=None), dict(suq=None), dict(wuq=None), dict(B=0), dict(eps=-1.0), dict(eps=float("nan"))):
+        assert qcall(**bad) == mfa.MFA_ERR_INVALID_ARG, bad
+    assert qcall(sdq=FAKE + 2) == mfa.MFA_ERR_ALIGNMENT
+    assert qcall(wdq=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert qcall(ws=None) == mfa.MFA_ERR_WORKSPACE
+    assert qcall(nbytes=mfa.mfa_qproj_workspace_size(2, mfa.MFA_BF16) - 1) == mfa.MFA_ERR_WORKSPACE
+    kv = mfa.raw_function("mfa_kv_append_w8")
+
+    def kcall(**kw):
+        a = dict(dict(dt=mfa.MFA_FP8_E4M3, sk=0.01, sv=0.02, ws=FAKE, nbytes=1 << 30, B=2), **kw)
+        ptrs = [a.get(n, FAKE) for n in ("x", "wk", "swk", "wv", "swv", "kc", "vc", "off", "len")]
+        return kv(*ptrs, a["dt"], a["sk"], a["sv"], a["ws"], a["nbytes"], a["B"], None)
+
+    assert kcall(swk=None) == mfa.MFA_ERR_INVALID_ARG
+    assert kcall(swv=None) == mfa.MFA_ERR_INVALID_ARG
+    assert kcall(B=mfa.MFA_MAX_BATCH + 1) == mfa.MFA_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-45):
+        assert kcall(sk=bad) == mfa.MFA_ERR_INVALID_ARG, bad
+        assert kcall(sv=bad) == mfa.MFA_ERR_INVALID_ARG, bad
+    # the cache scales are not read for a bf16 cache
+    assert kcall(dt=mfa.MFA_BF16, sk=0.0, ws=None) == mfa.MFA_ERR_WORKSPACE
+    assert kcall(dt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
+    assert kcall(swv=FAKE + 1) == mfa.MFA_ERR_ALIGNMENT
+    assert kcall(kc=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert kcall(nbytes=mfa.mfa_kv_append_workspace_size(2, mfa.MFA_BF16) - 1) == mfa.MFA_ERR_WORKSPACE
+    op = mfa.raw_function("mfa_oproj_w8")
+    assert op(FAKE, FAKE, None, FAKE, FAKE, 1 << 30, 2, None) == mfa.MFA_ERR_INVALID_ARG
+    assert op(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0, None) == mfa.MFA_ERR_INVALID_ARG
+    assert op(FAKE, FAKE, FAKE + 2, FAKE, FAKE, 1 << 30, 2, None) == mfa.MFA_ERR_ALIGNMENT
+    assert op(FAKE, MIS, FAKE, FAKE, FAKE, 1 << 30, 2, None) == mfa.MFA_ERR_ALIGNMENT
+    need = mfa.mfa_oproj_workspace_size(128, mfa.MFA_BF16)
+    if need > 0:
+        assert op(FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 128, None) == mfa.MFA_ERR_WORKSPACE
+
+
 def test_single_hip_runtime_in_process():
     # libmfa must bind to the HIP runtime torch already loaded, not a second copy
     maps = open(f"/proc/{os.getpid()}/maps").read()

@@ -7,6 +7,7 @@ oracle run from the stored inputs alone; "stage isolated" feeds the oracle's
 attention the GPU's own q and cache, so each kernel's error is seen alone.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -70,8 +71,14 @@ def _check_layer(inp, ids, kind, num_workgroups=0):
     offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
     o_iso, l_iso = om.decode_attn(qg, kc, vc, offs, lens)
     check(f"{kind} o (stage isolated)", runner.to_f64(call.o)[ids], o_iso, t["atol"], t["rel"])
-    y_iso = om.out_proj(runner.to_f64(call.o)[ids], om.to_f64(inp["w_o"], inp["kind_act"]))
+    y_iso = om.out_proj(runner.to_f64(call.o)[ids], _w_o(inp))
     check(f"{kind} y (stage isolated)", runner.to_f64(call.y)[ids], y_iso, t["atol"], t["rel"])
+
+
+def _w_o(inp):
+    if inp.get("kind_w") == gen.FP8_BLOCK:
+        return om.dequantize_blocks_e4m3fn(inp["w_o"], inp["w_o_scale"])
+    return om.to_f64(inp["w_o"], inp["kind_act"])
 
 
 def test_layer_tiny_fp32_full():
@@ -152,6 +159,31 @@ def test_layer_fp8_cache_small(G):
 def test_layer_fp8_cache_full():
     print("[case] layer layer_bf16_fp8kv_8k (full size, sampled sequences)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_bf16_fp8kv_8k"])
+    _check_layer_fp8(inp, [0, 64, 127])
+
+
+# ------------------------------------------------------------------ block-fp8 weights
+@pytest.mark.parametrize("kv", [gen.FP8, gen.BF16])
+def test_layer_block_fp8_weights_small(kv):
+    print(f"[case] layer block-fp8 weights, {kv} cache, B=5 ctx=300", flush=True)
+    w = dataclasses.replace(gen.scaled(gen.WORKLOADS["layer_fp8_8k"], batch=5, ctx=300), kv=kv)
+    inp = gen.make_layer(w)
+    if kv == gen.FP8:
+        _check_layer_fp8(inp, [0, 1, 2, 3, 4])
+    else:
+        _check_layer(inp, [0, 2, 4], "bf16")
+
+
+def test_layer_block_fp8_weights_batch_200():
+    # a second, partly filled 128-row batch chunk in every block-fp8 projection
+    print("[case] layer block-fp8 weights, bf16 cache, B=200 ctx=64", flush=True)
+    w = dataclasses.replace(gen.scaled(gen.WORKLOADS["layer_fp8_8k"], batch=200, ctx=64), kv=gen.BF16)
+    _check_layer(gen.make_layer(w), [0, 127, 128, 199], "bf16")
+
+
+def test_layer_block_fp8_full():
+    print("[case] layer layer_fp8_8k (full size, sampled sequences)", flush=True)
+    inp = gen.make_layer(gen.WORKLOADS["layer_fp8_8k"])
     _check_layer_fp8(inp, [0, 64, 127])
 
 

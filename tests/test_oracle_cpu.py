@@ -504,6 +504,76 @@ def test_layer_fp8_cache_stores_the_new_rows_quantized():
         assert np.allclose(outz["o"][b], oc * np.exp(lc - ln)[:, None], atol=1e-12)
 
 
+def test_block_fp8_weight_dequant_by_hand():
+    # a 256 x 384 weight: 2 x 3 blocks with distinct scales; each picked byte
+    # sits at a block corner so that a transposed or shifted block index fails
+    codes = np.zeros((256, 384), dtype=np.uint8)
+    scales = np.array([[0.5, 3.0, 1.0], [0.25, 7.0, 2.0 ** -8]], dtype=np.float32)
+    picks = {  # (row, col): (byte, value by hand)
+        (0, 0): (0x38, 0.5),          # 1.0 x 0.5
+        (127, 127): (0x40, 1.0),      # 2.0 x 0.5
+        (127, 128): (0x40, 6.0),      # 2.0 x 3   (block row 0, block col 1)
+        (128, 127): (0xB8, -0.25),    # -1.0 x 0.25 (block row 1, block col 0)
+        (128, 128): (0x3C, 10.5),     # 1.5 x 7
+        (200, 300): (0x7E, 1.75),     # 448 x 2^-8
+        (5, 383): (0x01, 2.0 ** -9),  # smallest subnormal x 1
+    }
+    for (r, c), (b, _) in picks.items():
+        codes[r, c] = b
+    w = om.dequantize_blocks_e4m3fn(codes, scales)
+    assert w.shape == (256, 384)
+    for (r, c), (_, v) in picks.items():
+        assert w[r, c] == v, (r, c, w[r, c], v)
+    assert np.count_nonzero(w) == len(picks)
+    with pytest.raises(ValueError):  # scales of the transposed grid do not fit
+        om.dequantize_blocks_e4m3fn(codes, scales.T)
+
+
+def test_block_fp8_generator_round_trip_through_oracle():
+    # generator quantizer (inputs) against the oracle's dequant: the amax of
+    # each block is stored as +-448 exactly, every value within half an e4m3
+    # step (2^-4 relative, 2^-10 x scale among subnormals), an all-zero block
+    # gets scale 1
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((256, 512)) * np.exp(rng.uniform(-3, 3, (256, 1)))).astype(np.float32)
+    w[128:, 384:] = 0
+    codes, sc = gen.quantize_blocks_e4m3fn(w)
+    assert codes.dtype == np.uint8 and sc.shape == (2, 4) and sc.dtype == np.float32
+    assert sc[1, 3] == 1.0
+    back = om.dequantize_blocks_e4m3fn(codes, sc)
+    for i in range(2):
+        for j in range(4):
+            blk = w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128].astype(np.float64)
+            bb = back[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            if i == 1 and j == 3:
+                assert not np.any(bb)
+                continue
+            k = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
+            assert abs(bb[k]) == 448.0 * float(sc[i, j]) and np.sign(bb[k]) == np.sign(blk[k])
+            err = np.abs(bb - blk)
+            assert np.all(err <= np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * float(sc[i, j])) * (1 + 1e-6))
+
+
+def test_layer_block_fp8_weights_use_the_dequantized_matrices():
+    # each of the five weights enters the layer as its block dequantization
+    # (a swapped scale table or weight role changes y)
+    inp = _small_layer(B=2, ctx=4)
+    q = {}
+    for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o"):
+        q[n], q[n + "_scale"] = gen.quantize_blocks_e4m3fn(inp[n])
+    blk = om.decode_layer(dict(inp, kind_w="fp8_block", **q))
+    ref = om.decode_layer(dict(inp, kind_w="f64", **{n: om.dequantize_blocks_e4m3fn(q[n], q[n + "_scale"])
+                                                   for n in ("w_dq", "w_uq", "w_k", "w_v", "w_o")}))
+    for key in ("c", "q", "k_new", "v_new", "o", "y"):
+        assert np.array_equal(blk[key], ref[key]), key
+    swapped = dict(inp, kind_w="fp8_block", **q)
+    swapped["w_k_scale"], swapped["w_v_scale"] = q["w_v_scale"] * 2, q["w_k_scale"]
+    assert not np.allclose(om.decode_layer(swapped)["y"], blk["y"])
+    # and the block-fp8 layer stays close to the float layer it stores
+    flt = om.decode_layer(inp)
+    assert np.max(np.abs(blk["y"] - flt["y"])) < 0.1 * np.max(np.abs(flt["y"]))
+
+
 def test_layer_attends_the_appended_row_and_nothing_beyond():
     inp = _small_layer()
     out = om.decode_layer(inp)
