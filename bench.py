@@ -11,7 +11,7 @@ already resident in HBM:
     pages in a shuffled order), one ``mfa_decode_attn_paged`` call;
   * ``*_mtp2`` attention workloads: two new query tokens per sequence
     (causal between them), one ``mfa_decode_attn_mt`` call; tokens/s counts
-    both;
+    both; ``*_paged_mtp2``: both, one ``mfa_decode_attn_paged_mt`` call;
   * ``layer_bf16_8k`` / ``layer_bf16_fp8kv_8k`` / ``layer_fp8_8k`` (block-fp8
     weights, e4m3 cache) / ``tiny_fp32``: the whole decode layer (q path, K/V
     append, attention, out-projection).
@@ -219,7 +219,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn_bf16_4k",
                     choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "attn_bf16_4k_paged",
-                             "attn_fp8kv_4k_paged", "attn_bf16_4k_mtp2", "attn_fp8kv_4k_mtp2", "layer_bf16_8k",
+                             "attn_fp8kv_4k_paged", "attn_bf16_4k_mtp2", "attn_fp8kv_4k_mtp2", "attn_bf16_4k_paged_mtp2",
+                             "attn_fp8kv_4k_paged_mtp2", "layer_bf16_8k",
                              "layer_bf16_fp8kv_8k", "layer_fp8_8k", "tiny_fp32"])
     ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -298,7 +299,8 @@ def main():
             # same call time as "achieved"; null when the kernel sources changed since the counters were taken
             "traffic": None if hbm_bytes is None else round(hbm_bytes / (ms * 1e-3) / 1e9, 2),
             "traffic_bytes_per_launch": hbm_bytes,
-            "kernel": ("mfa_decode_attn_paged" if "_paged" in res["workload"] else
+            "kernel": ("mfa_decode_attn_paged_mt" if "_paged_mtp2" in res["workload"] else
+                       "mfa_decode_attn_paged" if "_paged" in res["workload"] else
                        "mfa_decode_attn_mt" if "_mtp2" in res["workload"] else "mfa_decode_attn")
             + " call = attn_mfma_kernel + attn_combine_mfma_kernel (HIP events on the call's stream)"
             if w.kind == "attn" else "whole layer (HIP events)",

@@ -968,8 +968,9 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
       if (e == hipSuccess) e = launch(attn_combine_f32_kernel, comb_f32, block, stream, a);
       break;
     case AttnKind::BF16:
-      if (p.nt == 2)  // (contiguous cache only)
-        e = launch(attn_mfma_kernel<false, false, 2>, dim3(p.G), dim3(512), stream, a);
+      if (p.nt == 2)
+        e = p.table ? launch(attn_mfma_kernel<false, true, 2>, dim3(p.G), dim3(512), stream, a)
+                    : launch(attn_mfma_kernel<false, false, 2>, dim3(p.G), dim3(512), stream, a);
       else
         e = p.table ? launch(attn_mfma_kernel<false, true, 1>, dim3(p.G), block, stream, a)
                     : launch(attn_mfma_kernel<false, false, 1>, dim3(p.G), block, stream, a);
@@ -977,7 +978,8 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
       break;
     case AttnKind::BF16_FP8KV:
       if (p.nt == 2)
-        e = launch(attn_mfma_kernel<true, false, 2>, dim3(p.G), dim3(512), stream, a);
+        e = p.table ? launch(attn_mfma_kernel<true, true, 2>, dim3(p.G), dim3(512), stream, a)
+                    : launch(attn_mfma_kernel<true, false, 2>, dim3(p.G), dim3(512), stream, a);
       else
         e = p.table ? launch(attn_mfma_kernel<true, true, 1>, dim3(p.G), block, stream, a)
                     : launch(attn_mfma_kernel<true, false, 1>, dim3(p.G), block, stream, a);

@@ -299,7 +299,6 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
       return MFA_ERR_INVALID_ARG;
     while ((1 << page_shift) < page_rows) ++page_shift;
   }
-  if (n_tokens > 1 && paged) return MFA_ERR_UNSUPPORTED;
   mfa::AttnKind kind;
   if (q_dt == MFA_F32 && kv_dt == MFA_F32 && !paged && n_tokens == 1)
     kind = mfa::AttnKind::F32;
@@ -380,6 +379,16 @@ int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_page
                           int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream) {
   if (!block_table) return MFA_ERR_INVALID_ARG;
   return decode_attn_impl(q, k_pages, v_pages, nullptr, block_table, max_blocks, page_rows, seq_len, 1,
+                          softmax_scale, k_scale, v_scale, out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt,
+                          stream);
+}
+
+int mfa_decode_attn_paged_mt(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                             int max_blocks, int page_rows, const int32_t* seq_len, int n_tokens, float softmax_scale,
+                             float k_scale, float v_scale, void* out, float* lse, void* ws, size_t ws_bytes, int B,
+                             int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream) {
+  if (!block_table) return MFA_ERR_INVALID_ARG;
+  return decode_attn_impl(q, k_pages, v_pages, nullptr, block_table, max_blocks, page_rows, seq_len, n_tokens,
                           softmax_scale, k_scale, v_scale, out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt,
                           stream);
 }

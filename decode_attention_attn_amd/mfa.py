@@ -67,6 +67,9 @@ _lib.mfa_decode_attn_mt.restype = _I
 _lib.mfa_decode_attn_mt.argtypes = [_P, _P, _P, _P, _P, _I, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
 _lib.mfa_decode_attn_paged.restype = _I
 _lib.mfa_decode_attn_paged.argtypes = [_P, _P, _P, _P, _I, _I, _P, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
+_lib.mfa_decode_attn_paged_mt.restype = _I
+_lib.mfa_decode_attn_paged_mt.argtypes = [_P, _P, _P, _P, _I, _I, _P, _I, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I,
+                                          _P]
 _lib.mfa_qproj_w8.restype = _I
 _lib.mfa_qproj_w8.argtypes = [_P, _P, _P, _P, _F, _P, _P, _P, _P, _Z, _I, _P]
 _lib.mfa_kv_append_w8.restype = _I
@@ -82,7 +85,7 @@ EXPORTED = [
     "mfa_version", "mfa_status_string", "mfa_last_hip_error",
     "mfa_qproj_workspace_size", "mfa_qproj",
     "mfa_kv_append_workspace_size", "mfa_kv_append", "mfa_kv_append_fp8",
-    "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_paged",
+    "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_paged", "mfa_decode_attn_paged_mt",
     "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
     "mfa_oproj_workspace_size", "mfa_oproj",
     "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8",
@@ -190,6 +193,15 @@ def mfa_decode_attn_paged(q, k_pages, v_pages, block_table, max_blocks, page_row
                                       page_rows, _ptr(seq_len), softmax_scale, k_scale, v_scale, _ptr(out),
                                       _ptr(lse), _ptr(ws), _nbytes(ws), B, num_workgroups, q_dt, kv_dt,
                                       _stream(stream))
+
+
+def mfa_decode_attn_paged_mt(q, k_pages, v_pages, block_table, max_blocks, page_rows, seq_len, n_tokens,
+                             softmax_scale, k_scale, v_scale, out, lse, ws, B, num_workgroups, q_dt, kv_dt,
+                             stream=None) -> int:
+    return _lib.mfa_decode_attn_paged_mt(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), max_blocks,
+                                         page_rows, _ptr(seq_len), n_tokens, softmax_scale, k_scale, v_scale,
+                                         _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), B, num_workgroups, q_dt, kv_dt,
+                                         _stream(stream))
 
 
 def mfa_oproj_workspace_size(B: int, dt: int) -> int:

@@ -95,7 +95,13 @@ class AttnCall:
         d = self.dev
         k = d["k"] if k is None else k
         v = d["v"] if v is None else v
-        if d.get("table") is not None:
+        if d.get("table") is not None and d.get("nt", 1) > 1:
+            st = mfa.mfa_decode_attn_paged_mt(d["q"], k, v, d["table"], d["max_blocks"], d["page_rows"], d["len"],
+                                              d["nt"], SOFTMAX_SCALE, d["k_scale"], d["v_scale"], self.out, self.lse,
+                                              self.ws, d["B"], self.G, _DT[d["kind_q"]], _DT[d["kind_kv"]],
+                                              self.stream)
+            mfa.check(st, "mfa_decode_attn_paged_mt")
+        elif d.get("table") is not None:
             st = mfa.mfa_decode_attn_paged(d["q"], k, v, d["table"], d["max_blocks"], d["page_rows"], d["len"],
                                            SOFTMAX_SCALE, d["k_scale"], d["v_scale"], self.out, self.lse, self.ws,
                                            d["B"], self.G, _DT[d["kind_q"]], _DT[d["kind_kv"]], self.stream)

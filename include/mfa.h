@@ -182,6 +182,22 @@ int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_page
                           void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups,
                           mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
 
+/* ------------------------------------------------------------------ attention, paged cache, several new tokens
+ * Multi-token decode over a paged cache: the causal multi-token computation of
+ * mfa_decode_attn_mt, with sequence b's keys located through its block table
+ * as in mfa_decode_attn_paged (token t sees the first seq_len[b] -
+ * (n_tokens - 1 - t) keys of the sequence). Shapes, outputs, n_tokens
+ * (1 or 2), supported dtypes and the workspace size
+ * (mfa_decode_attn_mt_workspace_size) are those of mfa_decode_attn_mt; the
+ * page arguments and their preconditions are those of mfa_decode_attn_paged.
+ * block_table NULL: MFA_ERR_INVALID_ARG.
+ */
+int mfa_decode_attn_paged_mt(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                             int max_blocks, int page_rows, const int32_t* seq_len, int n_tokens,
+                             float softmax_scale, float k_scale, float v_scale, void* out, float* lse, void* ws,
+                             size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
+                             void* stream);
+
 /* ------------------------------------------------------------------ out-projection
  * y = O_flat W_o^T: attn [B, 16384] (the [B, 64, 256] attention output),
  * W_o [7168, 16384], y [B, 7168]. dt = MFA_F32 or MFA_BF16 (fp32 accumulation).

@@ -290,6 +290,28 @@ def decode_attn_paged(q, k_pages, v_pages, block_table, seq_len, page_rows, scal
     return np.stack(outs), np.stack(lses)
 
 
+def decode_attn_paged_mt(q, k_pages, v_pages, block_table, seq_len, page_rows, n_tokens, scale=SOFTMAX_SCALE,
+                         kind_q="f64", kind_kv="f64", k_scale=None, v_scale=None, batch_ids=None):
+    """decode_attn_mt over a paged cache: each sequence's keys are gathered from
+    its pages in block order (paged_rows), then the tokens attend causally
+    exactly as over a contiguous run. Returns (O [n_b, n, H, D], lse [n_b, n, H])."""
+    ids = list(range(len(seq_len))) if batch_ids is None else list(batch_ids)
+    kc, vc, off, lens = [], [], [], []
+    base = 0
+    for b in ids:
+        rows = paged_rows(block_table[b], seq_len[b], page_rows)
+        kc.append(np.asarray(k_pages)[rows])
+        vc.append(np.asarray(v_pages)[rows])
+        off.append(base)
+        lens.append(int(seq_len[b]))
+        base += len(rows)
+    k_run = np.concatenate(kc) if kc else np.asarray(k_pages)[:0]
+    v_run = np.concatenate(vc) if vc else np.asarray(v_pages)[:0]
+    qs = [q[b] for b in ids]
+    return decode_attn_mt(qs, k_run, v_run, np.asarray(off, dtype=np.int64), np.asarray(lens, dtype=np.int64),
+                          n_tokens, scale, kind_q=kind_q, kind_kv=kind_kv, k_scale=k_scale, v_scale=v_scale)
+
+
 # ------------------------------------------------------------------ output
 def out_proj(o, w_o):
     """y = O_flat W_o^T with O flattened head-major ([B, H*D])."""

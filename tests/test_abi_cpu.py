@@ -118,6 +118,28 @@ def test_decode_attn_mt_rejects_bad_arguments():
     assert call(nbytes=need2 - 1) == mfa.MFA_ERR_WORKSPACE
 
 
+def test_decode_attn_paged_mt_rejects_bad_arguments():
+    f = mfa.raw_function("mfa_decode_attn_paged_mt")
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, maxb=4, rows=64, len=FAKE, n=2, out=FAKE, ws=FAKE,
+                 nbytes=1 << 40, B=4, G=8, qdt=mfa.MFA_BF16, kvdt=mfa.MFA_FP8_E4M3)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["table"], a["maxb"], a["rows"], a["len"], a["n"], 0.0625, 1.0, 1.0,
+                 a["out"], None, a["ws"], a["nbytes"], a["B"], a["G"], a["qdt"], a["kvdt"], None)
+
+    assert call(table=None) == mfa.MFA_ERR_INVALID_ARG
+    for n in (0, 3):
+        assert call(n=n) == mfa.MFA_ERR_INVALID_ARG, n
+    assert call(maxb=0) == mfa.MFA_ERR_INVALID_ARG
+    assert call(rows=100) == mfa.MFA_ERR_INVALID_ARG
+    assert call(qdt=mfa.MFA_F32, kvdt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
+    assert call(qdt=mfa.MFA_FP8_E4M3) == mfa.MFA_ERR_UNSUPPORTED
+    assert call(len=FAKE + 2) == mfa.MFA_ERR_ALIGNMENT
+    assert call(ws=None) == mfa.MFA_ERR_WORKSPACE
+    assert call(nbytes=mfa.mfa_decode_attn_mt_workspace_size(4, 2, 8) - 1) == mfa.MFA_ERR_WORKSPACE
+
+
 def test_projections_reject_bad_arguments():
     qp = mfa.raw_function("mfa_qproj")
     assert qp(None, FAKE, None, 1e-6, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_F32, None) == mfa.MFA_ERR_INVALID_ARG

@@ -46,6 +46,38 @@ def test_two_tokens_small(kind, G):
     check_lse(f"two tokens lse {kind} G={G}", lse, l_ref, t["lse"])
 
 
+def _oracle_paged(pg, ids=None):
+    return om.decode_attn_paged_mt(pg["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], pg["seq_len"],
+                                   pg["page_rows"], pg["n_tokens"], kind_q=pg["kind_q"], kind_kv=pg["kind_kv"],
+                                   k_scale=pg["k_scale"], v_scale=pg["v_scale"], batch_ids=ids)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("page_rows,G", [(64, 1), (64, 0), (256, 3)])
+def test_two_tokens_paged_small(kind, page_rows, G):
+    # two tokens over shuffled pages whose unused rows hold NaN codes
+    print(f"[case] two tokens paged {kind} page_rows={page_rows} G={G} lengths={LENGTHS.tolist()}", flush=True)
+    w = gen.scaled(WL[kind], batch=len(LENGTHS), ctx=0, seed=4)
+    pg = gen.to_pages(gen.with_tokens(gen.make_attn(w, lengths=LENGTHS), 2), page_rows, seed=6)
+    _, out, lse = _run(pg, G)
+    o_ref, l_ref = _oracle_paged(pg)
+    t = TOL[kind]
+    check(f"two tokens paged out {kind} R={page_rows} G={G}", out, o_ref, t["atol"], t["rel"])
+    check_lse(f"two tokens paged lse {kind} R={page_rows} G={G}", lse, l_ref, t["lse"])
+
+
+@pytest.mark.parametrize("name,page_rows,ids", [("attn_bf16_4k", 64, [0, 15, 31]), ("attn_fp8kv_4k", 128, [0, 40, 63])])
+def test_two_tokens_paged_full_size(name, page_rows, ids):
+    print(f"[case] two tokens paged {name} page_rows={page_rows} (full size, sampled sequences)", flush=True)
+    w = gen.WORKLOADS[name]
+    pg = gen.to_pages(gen.with_tokens(gen.make_attn(w), 2), page_rows, seed=7)
+    _, out, lse = _run(pg)
+    o_ref, l_ref = _oracle_paged(pg, ids)
+    t = TOL[w.kv]
+    check(f"two tokens paged {name}", out[ids], o_ref, t["atol"], t["rel"])
+    check_lse(f"two tokens paged {name} lse", lse[ids], l_ref, t["lse"])
+
+
 @pytest.mark.parametrize("name,ids", [("attn_bf16_4k", [0, 15, 31]), ("attn_fp8kv_4k", [0, 31, 63])])
 def test_two_tokens_full_size(name, ids):
     print(f"[case] two tokens {name} (full size, sampled sequences)", flush=True)

@@ -336,6 +336,35 @@ def test_paged_attention_equals_the_contiguous_layout():
     assert np.allclose(o_p[b], bo, atol=1e-12) and np.allclose(l_p[b], bl, atol=1e-12)
 
 
+def test_paged_multi_token_equals_the_contiguous_layout():
+    # two new tokens over shuffled pages give the contiguous two-token result
+    # exactly; brute force from the pages pins the causal limit per token
+    rng = np.random.default_rng(6)
+    lens = np.array([1, 2, 9, 0, 17, 8], dtype=np.int32)
+    off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    q = rng.standard_normal((len(lens), 2, 4, 16))
+    k = rng.standard_normal((int(lens.sum()), 16))
+    v = rng.standard_normal((int(lens.sum()), 16))
+    inp = dict(q=q, k_cache=k, v_cache=v, seq_off=off, seq_len=lens, kind_kv="f32")
+    pg = gen.to_pages(inp, 8, seed=9)
+    o_c, l_c = om.decode_attn_mt(q, k, v, off, lens, 2, scale=0.25)
+    o_p, l_p = om.decode_attn_paged_mt(q, pg["k_pages"], pg["v_pages"], pg["block_table"], lens, 8, 2, scale=0.25)
+    assert o_p.shape == (6, 2, 4, 16) and l_p.shape == (6, 2, 4)
+    assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
+    # length 1: the first token sees nothing, the second sees the one row
+    assert not np.any(o_p[0, 0]) and np.all(l_p[0, 0] == -np.inf)
+    b = 4
+    rows = [int(pg["block_table"][b][j // 8]) * 8 + j % 8 for j in range(int(lens[b]))]
+    for t, m in ((0, 16), (1, 17)):
+        kr, vr = pg["k_pages"][rows[:m]].tolist(), pg["v_pages"][rows[:m]].tolist()
+        bo, bl = brute.mha(q[b, t].tolist(), [kr] * 4, [vr] * 4, 0.25)
+        assert np.allclose(o_p[b, t], bo, atol=1e-12) and np.allclose(l_p[b, t], bl, atol=1e-12)
+    # a subset of sequences equals the same rows of the whole batch
+    o_s, l_s = om.decode_attn_paged_mt(q, pg["k_pages"], pg["v_pages"], pg["block_table"], lens, 8, 2, scale=0.25,
+                                       batch_ids=[4, 1])
+    assert np.array_equal(o_s, o_p[[4, 1]]) and np.array_equal(l_s, l_p[[4, 1]])
+
+
 def test_empty_sequence_gives_zero_and_minus_inf():
     o, lse = om.attend_one(np.ones((64, 256)), np.zeros((0, 256)), np.zeros((0, 256)))
     assert np.all(o == 0) and np.all(np.isneginf(lse))
