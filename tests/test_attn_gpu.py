@@ -224,3 +224,56 @@ def test_full_attn_bf16_ragged():
     lens = gen.ragged_lengths(w.seed, w.batch, *w.ragged)
     ids = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7})
     _full("attn_bf16_ragged", ids)
+
+
+# ------------------------------------------------------------------ extremes
+@pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
+def test_single_long_sequence(kind):
+    # one sequence of 256K keys: every workgroup takes a piece of it and the
+    # combine merges one partial per workgroup (batches of 8, many rounds)
+    r = _runner()
+    print(f"[case] one sequence of 262144 keys, {kind}", flush=True)
+    inp = _make(kind, lengths=[262144], seed=5)
+    out, lse, _ = r.decode_attn(inp)
+    o_ref, l_ref = _oracle(inp)
+    t = TOL[kind]
+    check(f"long sequence out {kind}", r.to_f64(out), o_ref, t["atol"], t["rel"])
+    check_lse(f"long sequence lse {kind}", r.to_f64(lse), l_ref, t["lse"])
+
+
+def test_many_short_sequences():
+    # 4096 sequences of 0..40 keys: each workgroup walks across many whole
+    # sequences (every tile is a sequence's tail)
+    r = _runner()
+    lengths = np.random.default_rng(11).integers(0, 41, size=4096).astype(np.int32)
+    print(f"[case] 4096 sequences of 0..40 keys ({int((lengths == 0).sum())} empty)", flush=True)
+    inp = _make("bf16", lengths=lengths, seed=6)
+    out, lse, _ = r.decode_attn(inp)
+    o_ref, l_ref = _oracle(inp)
+    check("many short out", r.to_f64(out), o_ref, 2e-2, 1e-2)
+    check_lse("many short lse", r.to_f64(lse), l_ref, 2e-3)
+
+
+def test_maximum_batch():
+    # B = MFA_MAX_BATCH (65536): mostly one key per sequence (the output is
+    # then that V row bit for bit), a few longer and empty ones checked
+    # against the oracle
+    r = _runner()
+    B = 65536
+    lengths = np.ones(B, dtype=np.int32)
+    lengths[::4096] = 37
+    lengths[[5, 40000]] = 0
+    lengths[-1] = 300
+    print(f"[case] maximum batch B={B}", flush=True)
+    inp = _make("bf16", lengths=lengths, seed=7)
+    dev = r.upload_attn(inp)
+    out, lse = r.AttnCall(dev)()
+    torch.cuda.synchronize()
+    one = torch.as_tensor(np.nonzero(lengths == 1)[0], device=out.device)
+    rows = dev["off"][one]
+    want = dev["v"][rows].unsqueeze(1).expand(-1, 64, -1)
+    assert torch.equal(out[one], want), "L = 1 sequences must return their V row exactly"
+    ids = [0, 4096, 5, 40000, 65535, 12345]
+    o_ref, l_ref = _oracle(inp, ids)
+    check("maximum batch out", r.to_f64(out[ids]), o_ref, 2e-2, 1e-2)
+    check_lse("maximum batch lse", r.to_f64(lse[ids]), l_ref, 2e-3)
