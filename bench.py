@@ -167,6 +167,26 @@ def bench_layer(name, steps, warmup, graph=True):
                 inp=inp, w=w)
 
 
+def bench_probe(gib=4, reps=10):
+    """Achievable HBM read rate: mfa_bw_probe over a ``gib`` GiB buffer
+    (nontemporal 16-byte vector loads, one workgroup per CU), HIP events over ``reps``
+    calls after two warm-up calls."""
+    import torch
+
+    from decode_attention_attn_amd import mfa
+
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus, dtype=torch.int32, device="cuda")
+    ms = _event_time_ms(lambda i: mfa.check(mfa.mfa_bw_probe(buf, sink), "mfa_bw_probe"), reps, 2,
+                        torch.cuda.current_stream())
+    out = {"GBps": round(buf.numel() / (ms * 1e-3) / 1e9, 1), "bytes": buf.numel(), "ms": round(ms, 4),
+           "kernel": "mfa_bw_probe (nontemporal 16-byte vector loads, one workgroup per CU)"}
+    del buf, sink
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(res, seconds):
     """Time the float64 oracle on the host for about ``seconds`` on a sample of the workload."""
     import numpy as np
@@ -228,6 +248,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the fp8-KV 4K secondary measurement")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host instead of replaying "
                     "a captured HIP graph")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read bandwidth probe")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first copy this many MiB device-to-device three times (a plain copy kernel of known size, "
                     "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -254,6 +275,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    probe = None if args.no_probe else bench_probe()
     if args.workload.startswith("attn"):
         res = bench_attn(args.workload, args.steps, args.warmup, args.rotate, graph=not args.no_graph)
     else:
@@ -315,6 +337,12 @@ def main():
             "pct_of_peak_hbm": round(100 * s_gbps / HBM_PEAK_GBPS, 2),
             "tokens_per_s": round(sec["B"] / (sec["ms"] * 1e-3), 1)}}
         del sec
+    if probe is not None:
+        # the KV rate and the roofline's achieved rate as fractions of the
+        # measured streaming-read rate (the 8 TB/s peak stays the roofline)
+        line["bw_probe"] = probe
+        line["pct_of_probe"] = {"kv": round(100.0 * gbps / probe["GBps"], 2),
+                                "achieved": round(100.0 * achieved / probe["GBps"], 2)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmfa.so")
-SOURCES = ["attn.hip", "proj.hip", "mfa_api.cpp"]
+SOURCES = ["attn.hip", "proj.hip", "probe.hip", "mfa_api.cpp"]
 # Per-source extra flags. The attention kernels keep their accumulators in
 # ordinary VGPRs as MFMA operands: with accumulators in AGPRs the compiler
 # copied all of them to VGPRs on every loop iteration for the rarely taken

@@ -213,6 +213,11 @@ __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 __device__ __forceinline__ int swz_v16(int r) { return (r & 7) << 1; }
 __device__ __forceinline__ int swz_v8(int r) { return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3); }
 
+// Cache policy of the K/V tile DMAs: nontemporal (each cache byte is read
+// once per call). Measured on MI355X against the default policy: bf16 4K
+// 33.6 -> 33.1 us, fp8 4K -1 %, the 8K-64K ragged batch 123 -> 115 us.
+constexpr int kCpolNT = 2;
+
 // Direct-to-LDS DMA of the producer's current tile into a ring stage. Lane i of
 // a wave moves 16 bytes into LDS slot i of a 1 KB block, so the XOR swizzle is
 // applied on the global side: slot (row r, chunk pc) receives global chunk
@@ -247,9 +252,9 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
     const int ck = pc ^ swz_k(r32);
     const int cv = pc ^ (FP8 ? swz_v8(r32) : swz_v16(r32));
     __builtin_amdgcn_global_load_lds((const void*)(kb + (long long)rr * C::kRowBytes + ck * 16),
-                                     (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
+                                     (MFA_LDS void*)(stage + blk * 1024), 16, 0, kCpolNT);
     __builtin_amdgcn_global_load_lds((const void*)(vb + (long long)rr * C::kRowBytes + cv * 16),
-                                     (MFA_LDS void*)(stage + C::kHalfBytes + blk * 1024), 16, 0, 0);
+                                     (MFA_LDS void*)(stage + C::kHalfBytes + blk * 1024), 16, 0, kCpolNT);
   }
 }
 

@@ -449,4 +449,18 @@ int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, v
   return hip_status(mfa::launch_gemm(true, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s, s_o, s_o));
 }
 
+// ------------------------------------------------------------------ bandwidth probe
+int mfa_bw_probe(const void* buf, size_t bytes, uint32_t* sink, int num_workgroups, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || num_workgroups < 0 || num_workgroups > 65536)
+    return MFA_ERR_INVALID_ARG;
+  if (!aligned16(buf) || !aligned_n(sink, 4)) return MFA_ERR_ALIGNMENT;
+  int G = num_workgroups;
+  if (G == 0) {
+    int st = MFA_OK;
+    G = current_cu_count(&st);
+    if (st != MFA_OK) return st;
+  }
+  return hip_status(mfa::launch_bw_probe(buf, bytes, sink, G, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -61,6 +61,10 @@ inline size_t attn_ws_bytes(int B, int G, int nt = 1) { return attn_meta_offset(
 
 hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream);
 
+// Streaming-read probe: G workgroups XOR bytes / 16 16-byte words of buf,
+// one 32-bit checksum per workgroup into sink[G].
+hipError_t launch_bw_probe(const void* buf, size_t bytes, unsigned* sink, int G, hipStream_t stream);
+
 // ------------------------------------------------------------------ projections
 // Y[M, N] = X[M, K] * W^T where W = [W0 (N0 rows); W1 (N - N0 rows)], each [rows, K].
 enum class GemmOut {

@@ -76,6 +76,8 @@ _lib.mfa_kv_append_w8.restype = _I
 _lib.mfa_kv_append_w8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _F, _P, _Z, _I, _P]
 _lib.mfa_oproj_w8.restype = _I
 _lib.mfa_oproj_w8.argtypes = [_P, _P, _P, _P, _P, _Z, _I, _P]
+_lib.mfa_bw_probe.restype = _I
+_lib.mfa_bw_probe.argtypes = [_P, _Z, _P, _I, _P]
 _lib.mfa_oproj_workspace_size.restype = _Z
 _lib.mfa_oproj_workspace_size.argtypes = [_I, _I]
 _lib.mfa_oproj.restype = _I
@@ -88,7 +90,7 @@ EXPORTED = [
     "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_paged", "mfa_decode_attn_paged_mt",
     "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
     "mfa_oproj_workspace_size", "mfa_oproj",
-    "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8",
+    "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8", "mfa_bw_probe",
 ]
 
 
@@ -231,3 +233,7 @@ def mfa_kv_append_w8(x, w_k, s_k, w_v, s_v, k_cache, v_cache, seq_off, seq_len, 
 
 def mfa_oproj_w8(attn, w_o, s_o, y, ws, B, stream=None) -> int:
     return _lib.mfa_oproj_w8(_ptr(attn), _ptr(w_o), _ptr(s_o), _ptr(y), _ptr(ws), _nbytes(ws), B, _stream(stream))
+
+
+def mfa_bw_probe(buf, sink, num_workgroups=0, stream=None) -> int:
+    return _lib.mfa_bw_probe(_ptr(buf), _nbytes(buf), _ptr(sink), num_workgroups, _stream(stream))

@@ -231,6 +231,18 @@ int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const voi
 int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes,
                  int B, void* stream);
 
+/* ------------------------------------------------------------------ bandwidth probe
+ * Measures the achievable HBM read rate that the attention kernels' KV rate
+ * is compared with: num_workgroups workgroups (0: one per CU) read the
+ * bytes of buf (device, 16-byte aligned, bytes a non-zero multiple of 16)
+ * with 16-byte loads, and workgroup i writes the XOR of the 32-bit words it
+ * read to sink[i] (device uint32 array with num_workgroups entries, or one
+ * per CU when num_workgroups is 0). The XOR of all sink entries is the XOR
+ * of every 32-bit word of buf. Errors: MFA_ERR_INVALID_ARG (null pointer,
+ * bad size or count), MFA_ERR_ALIGNMENT.
+ */
+int mfa_bw_probe(const void* buf, size_t bytes, uint32_t* sink, int num_workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -226,6 +226,18 @@ def test_block_fp8_projections_reject_bad_arguments():
         assert op(FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 128, None) == mfa.MFA_ERR_WORKSPACE
 
 
+def test_bw_probe_rejects_bad_arguments():
+    f = mfa.raw_function("mfa_bw_probe")
+    assert f(None, 1024, FAKE, 8, None) == mfa.MFA_ERR_INVALID_ARG
+    assert f(FAKE, 1024, None, 8, None) == mfa.MFA_ERR_INVALID_ARG
+    for nbytes in (0, 8, 1000):
+        assert f(FAKE, nbytes, FAKE, 8, None) == mfa.MFA_ERR_INVALID_ARG, nbytes
+    for g in (-1, 65537):
+        assert f(FAKE, 1024, FAKE, g, None) == mfa.MFA_ERR_INVALID_ARG, g
+    assert f(MIS, 1024, FAKE, 8, None) == mfa.MFA_ERR_ALIGNMENT
+    assert f(FAKE, 1024, FAKE + 2, 8, None) == mfa.MFA_ERR_ALIGNMENT
+
+
 def test_single_hip_runtime_in_process():
     # libmfa must bind to the HIP runtime torch already loaded, not a second copy
     maps = open(f"/proc/{os.getpid()}/maps").read()
