@@ -73,6 +73,9 @@ def _kv_bytes(lengths, kv_kind):
     return int(np.asarray(lengths, dtype=np.int64).sum()) * per
 
 
+_SPREAD = {}  # per-call time percentiles of the last graph-timed run (ms)
+
+
 def _event_time_ms(fn, steps, warmup, stream, graph_calls=0):
     """Average time per step between HIP events on ``stream``.
 
@@ -97,14 +100,17 @@ def _event_time_ms(fn, steps, warmup, stream, graph_calls=0):
         for _ in range(2):
             g.replay()
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(reps):
+        # one event between replays: the mean over all of them, and the
+        # spread of per-call times replay by replay
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for r in range(reps):
             g.replay()
-        end.record(stream)
+            ev[r + 1].record(stream)
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / (reps * graph_calls)
+        per = sorted(ev[r].elapsed_time(ev[r + 1]) / graph_calls for r in range(reps))
+        _SPREAD.update(p10=per[int(0.1 * (reps - 1))], p50=per[(reps - 1) // 2], p90=per[int(0.9 * (reps - 1))])
+        return ev[0].elapsed_time(ev[reps]) / (reps * graph_calls)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -140,7 +146,8 @@ def bench_attn(name, steps, warmup, rotate, graph=True):
     B = w.batch
     kv = _kv_bytes(inp["seq_len"], w.kv)
     qo = 2 * nt * B * 64 * 256 * (4 if w.act == "f32" else 2)
-    return dict(workload=name, ms=ms, B=B, tokens=B * nt, kv_bytes=kv, alg_bytes=kv + qo, lengths=inp["seq_len"],
+    return dict(workload=name, ms=ms, spread=dict(_SPREAD) if graph else {}, B=B, tokens=B * nt, kv_bytes=kv,
+                alg_bytes=kv + qo, lengths=inp["seq_len"],
                 inp=inp, w=w)
 
 
@@ -163,7 +170,8 @@ def bench_layer(name, steps, warmup, graph=True):
     n_w = 2048 * 7168 + 16384 * 2048 + 2 * 256 * 7168 + 7168 * 16384
     # block-fp8 weights: one byte per element plus one fp32 scale per 128 x 128 block
     weights = n_w + 4 * (n_w // (128 * 128)) if w.weights == gen.FP8_BLOCK else n_w * esz
-    return dict(workload=name, ms=ms, B=B, kv_bytes=kv, alg_bytes=kv + weights, lengths=inp["seq_len"] + 1,
+    return dict(workload=name, ms=ms, spread=dict(_SPREAD) if graph else {}, B=B, kv_bytes=kv, alg_bytes=kv + weights,
+                lengths=inp["seq_len"] + 1,
                 inp=inp, w=w)
 
 
@@ -310,6 +318,8 @@ def main():
             "kv_buffer_sets": args.rotate if w.kind == "attn" else 1,
         },
         "tokens_per_s": round(res.get("tokens", w.batch) / (ms * 1e-3), 1),
+        # per-call time over each graph replay: 10th, 50th and 90th percentiles (ms)
+        "ms_per_step_pct": {k: round(v, 5) for k, v in res.get("spread", {}).items()} or None,
         "pct_of_peak_hbm": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
