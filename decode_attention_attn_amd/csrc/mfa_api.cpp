@@ -192,13 +192,15 @@ size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt) {
 }
 
 int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
-                  const int64_t* seq_off, const int32_t* seq_len, void* ws, size_t ws_bytes, int B, mfa_dtype act_dt,
+                  const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, void* ws, size_t ws_bytes, int B,
+                  mfa_dtype act_dt,
                   mfa_dtype cache_dt, void* stream) {
   if (!x || !w_k || !w_v || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 || B > MFA_MAX_BATCH)
     return MFA_ERR_INVALID_ARG;
   if (!act_dtype_ok(act_dt) || cache_dt != act_dt) return MFA_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
+      !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) ||
+      !aligned_n(seq_len_out, 4))
     return MFA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < kv_ws(B, act_dt, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
   mfa::GemmPlan plan;
@@ -209,12 +211,14 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
   if (e != hipSuccess) return hip_status(e);
-  e = mfa::launch_kv_scatter(bf, (const float*)ws, bf ? plan.splits : 1, B, k_cache, v_cache, seq_off, seq_len, s);
+  e = mfa::launch_kv_scatter(bf, (const float*)ws, bf ? plan.splits : 1, B, k_cache, v_cache, seq_off, seq_len,
+                             seq_len_out, s);
   return hip_status(e);
 }
 
 int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
-                      const int64_t* seq_off, const int32_t* seq_len, float k_scale, float v_scale, void* ws,
+                      const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
+                      float v_scale, void* ws,
                       size_t ws_bytes, int B, mfa_dtype act_dt, void* stream) {
   if (!x || !w_k || !w_v || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 || B > MFA_MAX_BATCH)
     return MFA_ERR_INVALID_ARG;
@@ -225,7 +229,8 @@ int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_c
     return MFA_ERR_INVALID_ARG;
   if (!act_dtype_ok(act_dt)) return MFA_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
+      !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) ||
+      !aligned_n(seq_len_out, 4))
     return MFA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < kv_ws(B, act_dt, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
   mfa::GemmPlan plan;
@@ -237,12 +242,13 @@ int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_c
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
   if (e != hipSuccess) return hip_status(e);
   e = mfa::launch_kv_scatter_fp8((const float*)ws, bf ? plan.splits : 1, B, k_cache, v_cache, seq_off, seq_len,
-                                 inv_k, inv_v, s);
+                                 inv_k, inv_v, seq_len_out, s);
   return hip_status(e);
 }
 
 int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const void* w_v, const float* s_v,
-                     void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len, mfa_dtype cache_dt,
+                     void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len,
+                     int32_t* seq_len_out, mfa_dtype cache_dt,
                      float k_scale, float v_scale, void* ws, size_t ws_bytes, int B, void* stream) {
   if (!x || !w_k || !s_k || !w_v || !s_v || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 ||
       B > MFA_MAX_BATCH)
@@ -254,7 +260,8 @@ int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const voi
               !isfinite(inv_k) || !isfinite(inv_v) || !(inv_k > 0.f) || !(inv_v > 0.f)))
     return MFA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(ws) || !aligned_n(s_k, 4) || !aligned_n(s_v, 4) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4))
+      !aligned16(ws) || !aligned_n(s_k, 4) || !aligned_n(s_v, 4) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) ||
+      !aligned_n(seq_len_out, 4))
     return MFA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < kv_ws(B, MFA_BF16, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
   mfa::GemmPlan plan;
@@ -265,8 +272,9 @@ int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const voi
   hipError_t e = mfa::launch_gemm(true, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s, s_k, s_v);
   if (e != hipSuccess) return hip_status(e);
   e = fp8 ? mfa::launch_kv_scatter_fp8((const float*)ws, plan.splits, B, k_cache, v_cache, seq_off, seq_len, inv_k,
-                                       inv_v, s)
-          : mfa::launch_kv_scatter(true, (const float*)ws, plan.splits, B, k_cache, v_cache, seq_off, seq_len, s);
+                                       inv_v, seq_len_out, s)
+          : mfa::launch_kv_scatter(true, (const float*)ws, plan.splits, B, k_cache, v_cache, seq_off, seq_len,
+                                   seq_len_out, s);
   return hip_status(e);
 }
 

@@ -94,10 +94,10 @@ hipError_t launch_rmsnorm_reduce(bool bf16, const float* part, int S, int M, int
 hipError_t launch_sum_reduce(bool bf16, const float* part, int S, int M, int N, void* out, hipStream_t stream);
 // rows m: k = sum_s part[s][m][0:256], v = sum_s part[s][m][256:512] written at cache row off[m] + len[m].
 hipError_t launch_kv_scatter(bool bf16, const float* part, int S, int M, void* k_cache, void* v_cache,
-                             const int64_t* seq_off, const int32_t* seq_len, hipStream_t stream);
+                             const int64_t* seq_off, const int32_t* seq_len, int32_t* len_out, hipStream_t stream);
 // rows into e4m3 caches: byte = e4m3(clamp(x * inv, +-448)), round to nearest even
 hipError_t launch_kv_scatter_fp8(const float* part, int S, int M, void* k_cache, void* v_cache,
                                  const int64_t* seq_off, const int32_t* seq_len, float inv_k, float inv_v,
-                                 hipStream_t stream);
+                                 int32_t* len_out, hipStream_t stream);
 
 }  // namespace mfa

@@ -351,18 +351,31 @@ __global__ __launch_bounds__(256) void sum_reduce_kernel(const float* part, int 
   dst[3] = (OutT)v[3];
 }
 
+// The length including the appended row, for the attention call that
+// follows: written once every thread of the row's workgroup has read the old
+// length (len_out may be seq_len itself: an in-place increment).
+__device__ __forceinline__ void write_len_out(int32_t* len_out, int m, int32_t len) {
+  if (len_out != nullptr) {
+    __syncthreads();
+    if (threadIdx.x == 0) len_out[m] = len + 1;
+  }
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(128) void kv_scatter_kernel(const float* part, int S, int M, OutT* kc, OutT* vc,
-                                                         const int64_t* seq_off, const int32_t* seq_len) {
+                                                         const int64_t* seq_off, const int32_t* seq_len,
+                                                         int32_t* len_out) {
   const int m = blockIdx.x;
   const int col = 4 * threadIdx.x;  // 0..508 of the [k | v] row
   const f32x4 v = sum_splits(part + (long long)m * 512 + col, (long long)M * 512, S);
-  const long long row = seq_off[m] + (long long)seq_len[m];
+  const int32_t len = seq_len[m];
+  const long long row = seq_off[m] + (long long)len;
   OutT* dst = (col < 256 ? kc : vc) + row * 256 + (col & 255);
   dst[0] = (OutT)v[0];
   dst[1] = (OutT)v[1];
   dst[2] = (OutT)v[2];
   dst[3] = (OutT)v[3];
+  write_len_out(len_out, m, len);
 }
 
 // The same rows into an e4m3 cache: stored byte = e4m3(x / scale) with round to
@@ -370,7 +383,8 @@ __global__ __launch_bounds__(128) void kv_scatter_kernel(const float* part, int 
 // on the host) and clamped to the largest finite magnitude, 448 (NaN stays NaN).
 __global__ __launch_bounds__(128) void kv_scatter_fp8_kernel(const float* part, int S, int M, unsigned char* kc,
                                                              unsigned char* vc, const int64_t* seq_off,
-                                                             const int32_t* seq_len, float inv_k, float inv_v) {
+                                                             const int32_t* seq_len, float inv_k, float inv_v,
+                                                             int32_t* len_out) {
   const int m = blockIdx.x;
   const int col = 4 * threadIdx.x;  // 0..508 of the [k | v] row
   const f32x4 v = sum_splits(part + (long long)m * 512 + col, (long long)M * 512, S);
@@ -383,8 +397,10 @@ __global__ __launch_bounds__(128) void kv_scatter_fp8_kernel(const float* part, 
   }
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);  // bytes 0, 1
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);       // bytes 2, 3
-  const long long row = seq_off[m] + (long long)seq_len[m];
+  const int32_t len = seq_len[m];
+  const long long row = seq_off[m] + (long long)len;
   *(int*)((col < 256 ? kc : vc) + row * 256 + (col & 255)) = w;
+  write_len_out(len_out, m, len);
 }
 
 // ------------------------------------------------------------------ host side
@@ -467,20 +483,20 @@ hipError_t launch_sum_reduce(bool bf16_path, const float* part, int S, int M, in
 }
 
 hipError_t launch_kv_scatter(bool bf16_path, const float* part, int S, int M, void* k_cache, void* v_cache,
-                             const int64_t* seq_off, const int32_t* seq_len, hipStream_t stream) {
+                             const int64_t* seq_off, const int32_t* seq_len, int32_t* len_out, hipStream_t stream) {
   if (bf16_path)
     return launch(kv_scatter_kernel<bf16>, dim3(M), dim3(128), stream, part, S, M, (bf16*)k_cache,
-                       (bf16*)v_cache, seq_off, seq_len);
+                       (bf16*)v_cache, seq_off, seq_len, len_out);
   else
     return launch(kv_scatter_kernel<float>, dim3(M), dim3(128), stream, part, S, M, (float*)k_cache,
-                       (float*)v_cache, seq_off, seq_len);
+                       (float*)v_cache, seq_off, seq_len, len_out);
 }
 
 hipError_t launch_kv_scatter_fp8(const float* part, int S, int M, void* k_cache, void* v_cache,
                                  const int64_t* seq_off, const int32_t* seq_len, float inv_k, float inv_v,
-                                 hipStream_t stream) {
+                                 int32_t* len_out, hipStream_t stream) {
   return launch(kv_scatter_fp8_kernel, dim3(M), dim3(128), stream, part, S, M, (unsigned char*)k_cache,
-                (unsigned char*)v_cache, seq_off, seq_len, inv_k, inv_v);
+                (unsigned char*)v_cache, seq_off, seq_len, inv_k, inv_v, len_out);
 }
 
 }  // namespace mfa

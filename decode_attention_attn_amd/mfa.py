@@ -54,9 +54,9 @@ _lib.mfa_qproj.argtypes = [_P, _P, _P, _F, _P, _P, _P, _Z, _I, _I, _P]
 _lib.mfa_kv_append_workspace_size.restype = _Z
 _lib.mfa_kv_append_workspace_size.argtypes = [_I, _I]
 _lib.mfa_kv_append.restype = _I
-_lib.mfa_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]
+_lib.mfa_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]
 _lib.mfa_kv_append_fp8.restype = _I
-_lib.mfa_kv_append_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _Z, _I, _I, _P]
+_lib.mfa_kv_append_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _Z, _I, _I, _P]
 _lib.mfa_decode_attn_workspace_size.restype = _Z
 _lib.mfa_decode_attn_workspace_size.argtypes = [_I, _I]
 _lib.mfa_decode_attn.restype = _I
@@ -73,7 +73,7 @@ _lib.mfa_decode_attn_paged_mt.argtypes = [_P, _P, _P, _P, _I, _I, _P, _I, _F, _F
 _lib.mfa_qproj_w8.restype = _I
 _lib.mfa_qproj_w8.argtypes = [_P, _P, _P, _P, _F, _P, _P, _P, _P, _Z, _I, _P]
 _lib.mfa_kv_append_w8.restype = _I
-_lib.mfa_kv_append_w8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _F, _P, _Z, _I, _P]
+_lib.mfa_kv_append_w8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _F, _P, _Z, _I, _P]
 _lib.mfa_oproj_w8.restype = _I
 _lib.mfa_oproj_w8.argtypes = [_P, _P, _P, _P, _P, _Z, _I, _P]
 _lib.mfa_bw_probe.restype = _I
@@ -155,16 +155,18 @@ def mfa_kv_append_workspace_size(B: int, act_dt: int) -> int:
     return _lib.mfa_kv_append_workspace_size(B, act_dt)
 
 
-def mfa_kv_append(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, ws, B, act_dt, cache_dt, stream=None) -> int:
+def mfa_kv_append(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, ws, B, act_dt, cache_dt, stream=None,
+                  seq_len_out=None) -> int:
     return _lib.mfa_kv_append(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off),
-                              _ptr(seq_len), _ptr(ws), _nbytes(ws), B, act_dt, cache_dt, _stream(stream))
+                              _ptr(seq_len), _ptr(seq_len_out), _ptr(ws), _nbytes(ws), B, act_dt, cache_dt,
+                              _stream(stream))
 
 
 def mfa_kv_append_fp8(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, k_scale, v_scale, ws, B, act_dt,
-                      stream=None) -> int:
+                      stream=None, seq_len_out=None) -> int:
     return _lib.mfa_kv_append_fp8(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off),
-                                  _ptr(seq_len), float(k_scale), float(v_scale), _ptr(ws), _nbytes(ws), B, act_dt,
-                                  _stream(stream))
+                                  _ptr(seq_len), _ptr(seq_len_out), float(k_scale), float(v_scale), _ptr(ws),
+                                  _nbytes(ws), B, act_dt, _stream(stream))
 
 
 def mfa_decode_attn_workspace_size(B: int, num_workgroups: int = 0) -> int:
@@ -225,10 +227,10 @@ def mfa_qproj_w8(x, w_dq, s_dq, gamma, eps, w_uq, s_uq, q_out, ws, B, stream=Non
 
 
 def mfa_kv_append_w8(x, w_k, s_k, w_v, s_v, k_cache, v_cache, seq_off, seq_len, cache_dt, k_scale, v_scale, ws, B,
-                     stream=None) -> int:
+                     stream=None, seq_len_out=None) -> int:
     return _lib.mfa_kv_append_w8(_ptr(x), _ptr(w_k), _ptr(s_k), _ptr(w_v), _ptr(s_v), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(seq_off), _ptr(seq_len), cache_dt, float(k_scale), float(v_scale), _ptr(ws),
-                                 _nbytes(ws), B, _stream(stream))
+                                 _ptr(seq_off), _ptr(seq_len), _ptr(seq_len_out), cache_dt, float(k_scale),
+                                 float(v_scale), _ptr(ws), _nbytes(ws), B, _stream(stream))
 
 
 def mfa_oproj_w8(attn, w_o, s_o, y, ws, B, stream=None) -> int:

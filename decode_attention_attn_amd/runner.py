@@ -178,12 +178,12 @@ class LayerCall:
                   "mfa_qproj")
         if d["kind_kv"] == FP8:
             mfa.check(mfa.mfa_kv_append_fp8(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"],
-                                            d["k_scale"], d["v_scale"], self.ws_kv, B, dt, s), "mfa_kv_append_fp8")
+                                            d["k_scale"], d["v_scale"], self.ws_kv, B, dt, s,
+                                            seq_len_out=self.len_after), "mfa_kv_append_fp8")
         else:
             mfa.check(mfa.mfa_kv_append(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"], self.ws_kv,
-                                        B, dt, _DT[d["kind_kv"]], s), "mfa_kv_append")
-        # the appended row is attended: length + 1 (the caller owns seq_len)
-        torch.add(d["len"], 1, out=self.len_after)
+                                        B, dt, _DT[d["kind_kv"]], s, seq_len_out=self.len_after), "mfa_kv_append")
+        # the appended row is attended: the append wrote len + 1 into len_after
         mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
                                       d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
                                       _DT[d["kind_kv"]], s),
@@ -200,8 +200,7 @@ class LayerCall:
                                    self.q, self.ws_q, B, s), "mfa_qproj_w8")
         mfa.check(mfa.mfa_kv_append_w8(d["x"], d["w_k"], d["w_k_scale"], d["w_v"], d["w_v_scale"], d["k"], d["v"],
                                        d["off"], d["len"], _DT[d["kind_kv"]], d["k_scale"], d["v_scale"],
-                                       self.ws_kv, B, s), "mfa_kv_append_w8")
-        torch.add(d["len"], 1, out=self.len_after)
+                                       self.ws_kv, B, s, seq_len_out=self.len_after), "mfa_kv_append_w8")
         mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
                                       d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
                                       _DT[d["kind_kv"]], s),

@@ -88,16 +88,19 @@ int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, co
  * The new token's shared K and V rows (Step-3 summary, "Method": one K and one
  * V per token): k = x W_k^T, v = x W_v^T (W_k, W_v [256, 7168]), written to
  * rows seq_off[b] + seq_len[b] of k_cache / v_cache ([rows, 256], cache_dt).
- * seq_off (int64) and seq_len (int32) are device arrays of length B; seq_len
- * is NOT modified (the caller advances it before attending). Supported:
+ * seq_off (int64) and seq_len (int32) are device arrays of length B.
+ * seq_len_out: NULL, or a device int32 array of length B (4-byte aligned)
+ * that receives seq_len[b] + 1, the length including the appended row, for
+ * the attention call that follows; it may be seq_len itself (an in-place
+ * increment, done after the row is written). Supported:
  * act_dt = cache_dt = MFA_F32, or act_dt = cache_dt = MFA_BF16.
  * Device-side precondition: the target rows exist and are distinct.
  * ws: at least mfa_kv_append_workspace_size(B, act_dt) bytes.
  */
 size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt);
 int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
-                  const int64_t* seq_off, const int32_t* seq_len, void* ws, size_t ws_bytes, int B,
-                  mfa_dtype act_dt, mfa_dtype cache_dt, void* stream);
+                  const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, void* ws, size_t ws_bytes,
+                  int B, mfa_dtype act_dt, mfa_dtype cache_dt, void* stream);
 
 /* ------------------------------------------------------------------ K/V append, e4m3 cache
  * As mfa_kv_append, but the rows are stored quantized into e4m3 caches (the
@@ -113,8 +116,8 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
  * bytes. Same device-side precondition as mfa_kv_append.
  */
 int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
-                      const int64_t* seq_off, const int32_t* seq_len, float k_scale, float v_scale,
-                      void* ws, size_t ws_bytes, int B, mfa_dtype act_dt, void* stream);
+                      const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
+                      float v_scale, void* ws, size_t ws_bytes, int B, mfa_dtype act_dt, void* stream);
 
 /* ------------------------------------------------------------------ attention
  * Shared-KV decode attention (Step-3 summary, "Key claims"/"Method": 64 query
@@ -226,8 +229,8 @@ int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float
                  void* stream);
 int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const void* w_v, const float* s_v,
                      void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len,
-                     mfa_dtype cache_dt, float k_scale, float v_scale, void* ws, size_t ws_bytes, int B,
-                     void* stream);
+                     int32_t* seq_len_out, mfa_dtype cache_dt, float k_scale, float v_scale, void* ws,
+                     size_t ws_bytes, int B, void* stream);
 int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes,
                  int B, void* stream);
 

@@ -149,18 +149,20 @@ def test_projections_reject_bad_arguments():
     need = mfa.mfa_qproj_workspace_size(2, mfa.MFA_BF16)
     assert qp(FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, need - 1, 2, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
     kv = mfa.raw_function("mfa_kv_append")
-    args = [FAKE] * 8
+    args = [FAKE] * 7 + [None, FAKE]  # x, w_k, w_v, k, v, off, len, len_out (none), ws
     assert kv(*args, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_FP8_E4M3, None) == mfa.MFA_ERR_UNSUPPORTED
     assert kv(*args, 1 << 30, 2, mfa.MFA_F32, mfa.MFA_BF16, None) == mfa.MFA_ERR_UNSUPPORTED
-    assert kv(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_BF16,
+    assert kv(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_BF16,
               None) == mfa.MFA_ERR_INVALID_ARG
+    assert kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, 1 << 30, 2, mfa.MFA_BF16, mfa.MFA_BF16,
+              None) == mfa.MFA_ERR_ALIGNMENT  # a misaligned seq_len_out
     assert kv(*args, 0, 2, mfa.MFA_BF16, mfa.MFA_BF16, None) == mfa.MFA_ERR_WORKSPACE
     k8 = mfa.raw_function("mfa_kv_append_fp8")
     ok = dict(sk=0.01, sv=0.02, ws=FAKE, nbytes=1 << 30, B=2, dt=mfa.MFA_BF16)
 
     def k8call(**kw):
         a = dict(ok, **kw)
-        ptrs = [a.get(n, FAKE) for n in ("x", "wk", "wv", "kc", "vc", "off", "len")]
+        ptrs = [a.get(n, FAKE) for n in ("x", "wk", "wv", "kc", "vc", "off", "len")] + [a.get("lout")]
         return k8(*ptrs, a["sk"], a["sv"], a["ws"], a["nbytes"], a["B"], a["dt"], None)
 
     assert k8call(kc=None) == mfa.MFA_ERR_INVALID_ARG
@@ -171,6 +173,7 @@ def test_projections_reject_bad_arguments():
     assert k8call(dt=mfa.MFA_FP8_E4M3) == mfa.MFA_ERR_UNSUPPORTED
     assert k8call(vc=MIS) == mfa.MFA_ERR_ALIGNMENT
     assert k8call(off=FAKE + 4) == mfa.MFA_ERR_ALIGNMENT
+    assert k8call(lout=FAKE + 2) == mfa.MFA_ERR_ALIGNMENT
     assert k8call(ws=None) == mfa.MFA_ERR_WORKSPACE
     assert k8call(nbytes=mfa.mfa_kv_append_workspace_size(2, mfa.MFA_BF16) - 1) == mfa.MFA_ERR_WORKSPACE
     op = mfa.raw_function("mfa_oproj")
@@ -201,7 +204,7 @@ def test_block_fp8_projections_reject_bad_arguments():
 
     def kcall(**kw):
         a = dict(dict(dt=mfa.MFA_FP8_E4M3, sk=0.01, sv=0.02, ws=FAKE, nbytes=1 << 30, B=2), **kw)
-        ptrs = [a.get(n, FAKE) for n in ("x", "wk", "swk", "wv", "swv", "kc", "vc", "off", "len")]
+        ptrs = [a.get(n, FAKE) for n in ("x", "wk", "swk", "wv", "swv", "kc", "vc", "off", "len")] + [a.get("lout")]
         return kv(*ptrs, a["dt"], a["sk"], a["sv"], a["ws"], a["nbytes"], a["B"], None)
 
     assert kcall(swk=None) == mfa.MFA_ERR_INVALID_ARG
@@ -215,6 +218,7 @@ def test_block_fp8_projections_reject_bad_arguments():
     assert kcall(dt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
     assert kcall(swv=FAKE + 1) == mfa.MFA_ERR_ALIGNMENT
     assert kcall(kc=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert kcall(lout=FAKE + 1) == mfa.MFA_ERR_ALIGNMENT
     assert kcall(nbytes=mfa.mfa_kv_append_workspace_size(2, mfa.MFA_BF16) - 1) == mfa.MFA_ERR_WORKSPACE
     op = mfa.raw_function("mfa_oproj_w8")
     assert op(FAKE, FAKE, None, FAKE, FAKE, 1 << 30, 2, None) == mfa.MFA_ERR_INVALID_ARG

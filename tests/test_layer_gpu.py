@@ -37,6 +37,8 @@ def _run_layer(inp, num_workgroups=0):
 
 def _check_layer(inp, ids, kind, num_workgroups=0):
     runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups)
+    # the append hands attention the length including the new row
+    assert torch.equal(call.len_after, dev["len"] + 1)
     t = TOL[kind]
     ref = om.decode_layer(inp, batch_ids=ids)
     B = len(inp["seq_len"])
@@ -221,6 +223,41 @@ def test_layer_block_fp8_full():
     print("[case] layer layer_fp8_8k (full size, sampled sequences)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_fp8_8k"])
     _check_layer_fp8(inp, [0, 64, 127])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_kv_append_in_place_length_increment(kv):
+    # seq_len_out = seq_len: each row goes to its sequence's old length, then
+    # the length advances by one
+    from decode_attention_attn_amd import mfa, runner
+
+    print(f"[case] kv append with an in-place length increment, {kv} cache", flush=True)
+    wl = "layer_bf16_8k" if kv == "bf16" else "layer_bf16_fp8kv_8k"
+    inp = gen.make_layer(gen.scaled(gen.WORKLOADS[wl], batch=6, ctx=50))
+    dev = runner.upload_layer(inp)
+    B = 6
+    ws = torch.empty(mfa.mfa_kv_append_workspace_size(B, mfa.MFA_BF16), dtype=torch.uint8, device="cuda")
+    old = dev["len"].clone()
+    if kv == "bf16":
+        st = mfa.mfa_kv_append(dev["x"], dev["w_k"], dev["w_v"], dev["k"], dev["v"], dev["off"], dev["len"], ws, B,
+                               mfa.MFA_BF16, mfa.MFA_BF16, seq_len_out=dev["len"])
+    else:
+        st = mfa.mfa_kv_append_fp8(dev["x"], dev["w_k"], dev["w_v"], dev["k"], dev["v"], dev["off"], dev["len"],
+                                   dev["k_scale"], dev["v_scale"], ws, B, mfa.MFA_BF16, seq_len_out=dev["len"])
+    mfa.check(st, "kv append")
+    torch.cuda.synchronize()
+    assert torch.equal(dev["len"], old + 1)
+    ref = om.decode_layer(inp)
+    rows = torch.as_tensor((inp["seq_off"] + inp["seq_len"]).astype(np.int64), device=dev["k"].device)
+    if kv == "bf16":
+        t = TOL["bf16"]
+        check("in-place k_new", runner.to_f64(dev["k"][rows]), ref["k_new"], t["atol"], t["rel"])
+        check("in-place v_new", runner.to_f64(dev["v"][rows]), ref["v_new"], t["atol"], t["rel"])
+    else:
+        _check_codes("in-place k codes", dev["k"][rows].cpu().numpy(), ref["k_new_codes"], ref["k_new"],
+                     inp["k_scale"])
+        _check_codes("in-place v codes", dev["v"][rows].cpu().numpy(), ref["v_new_codes"], ref["v_new"],
+                     inp["v_scale"])
 
 
 def test_kv_append_fp8_f32_activations_and_saturation():
