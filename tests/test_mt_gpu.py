@@ -105,3 +105,25 @@ def test_one_token_through_the_multi_token_entry_is_the_single_token_call():
                                      lse, ws, B, 0, mfa.MFA_BF16, mfa.MFA_BF16), "mfa_decode_attn_mt")
     torch.cuda.synchronize()
     assert torch.equal(out, o1) and torch.equal(lse, l1)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
+def test_one_token_through_the_paged_multi_token_entry_is_the_paged_call(kind):
+    print(f"[case] n_tokens = 1 via mfa_decode_attn_paged_mt vs mfa_decode_attn_paged, {kind}", flush=True)
+    from decode_attention_attn_amd import mfa, runner
+
+    w = gen.scaled(WL[kind], batch=6, ctx=0, seed=8)
+    pg = gen.to_pages(gen.make_attn(w, lengths=np.array([3000, 17, 1500, 4096, 0, 129], dtype=np.int32)), 64,
+                      seed=9)
+    dev = runner.upload_attn(pg)
+    o1, l1 = runner.AttnCall(dev)()
+    B = dev["B"]
+    out = torch.empty_like(o1)
+    lse = torch.empty_like(l1)
+    ws = torch.empty(mfa.mfa_decode_attn_mt_workspace_size(B, 1, 0), dtype=torch.uint8, device="cuda")
+    mfa.check(mfa.mfa_decode_attn_paged_mt(dev["q"], dev["k"], dev["v"], dev["table"], dev["max_blocks"],
+                                           dev["page_rows"], dev["len"], 1, 0.0625, dev["k_scale"], dev["v_scale"],
+                                           out, lse, ws, B, 0, mfa.MFA_BF16, runner.dtype_code(kind)),
+              "mfa_decode_attn_paged_mt")
+    torch.cuda.synchronize()
+    assert torch.equal(out, o1) and torch.equal(lse, l1)
