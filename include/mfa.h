@@ -113,7 +113,8 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
  * v_scale are host values, finite, > 0, with finite reciprocals (else
  * MFA_ERR_INVALID_ARG). act_dt = MFA_F32 or MFA_BF16. Caches [rows, 256]
  * bytes, 16-byte aligned. ws: at least mfa_kv_append_workspace_size(B, act_dt)
- * bytes. Same device-side precondition as mfa_kv_append.
+ * bytes. seq_off, seq_len, seq_len_out and the device-side precondition as
+ * for mfa_kv_append.
  */
 int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
                       const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
@@ -221,7 +222,8 @@ int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_by
  * and each 64-wide slice of a block is scaled in fp32). Workspace sizes are
  * those of the bf16 calls (mfa_qproj_workspace_size(B, MFA_BF16), ...).
  * mfa_kv_append_w8 writes a bf16 cache (cache_dt = MFA_BF16, scales unused)
- * or an e4m3 cache as mfa_kv_append_fp8 does (cache_dt = MFA_FP8_E4M3).
+ * or an e4m3 cache as mfa_kv_append_fp8 does (cache_dt = MFA_FP8_E4M3);
+ * seq_len_out as for mfa_kv_append.
  * Scale arrays: device fp32, 4-byte aligned.
  */
 int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps,
