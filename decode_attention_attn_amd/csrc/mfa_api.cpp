@@ -54,17 +54,13 @@ int current_cu_count(int* status) {
 
 bool act_dtype_ok(mfa_dtype dt) { return dt == MFA_F32 || dt == MFA_BF16; }
 
-size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-
-// Compute units the projection plans are made for. Workspace sizes assume this
-// many (no device needed to size a workspace); a call plans for
-// min(device CUs, kPlanCus), and its split-K factor never exceeds the sized
-// one because it only grows with the CU count.
-constexpr int kPlanCus = 256;
+// Compute units a call's projection plans are made for: the device's, at
+// most mfa::kPlanCus. Workspace sizes need no device: they reserve the
+// partial-sum bytes that bound the plan of every CU count up to kPlanCus
+// (mfa::gemm_partial_bound), and each call checks its own plan against that.
 int plan_cus(int* status) {
-  if (status == nullptr) return kPlanCus;
   const int c = current_cu_count(status);
-  return c < kPlanCus ? c : kPlanCus;
+  return c < mfa::kPlanCus ? c : mfa::kPlanCus;
 }
 
 
@@ -90,24 +86,43 @@ const char* mfa_status_string(int status) {
 
 // ------------------------------------------------------------------ q path
 // Workspace: partial sums (those of the down-projection, later reused by the
-// up-projection's), then the normalized latent c_hat. 0 on a device error.
-static size_t qproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* dn_out, mfa::GemmPlan* up_out, int* status) {
-  const bool bf = dt == MFA_BF16;
-  const int cus = plan_cus(status);
-  if (cus <= 0) return 0;
-  const mfa::GemmPlan dn = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK, cus);
-  const mfa::GemmPlan up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus);
-  if (dn_out) *dn_out = dn;
-  if (up_out) *up_out = up;
-  size_t part = bf ? mfa::gemm_partial_bytes(dn) : (size_t)B * MFA_RANK * sizeof(float);
-  if (bf && up.splits > 1 && mfa::gemm_partial_bytes(up) > part) part = mfa::gemm_partial_bytes(up);
-  const size_t chat = (size_t)B * MFA_RANK * (bf ? 2 : 4);
-  return align256(part) + align256(chat);
-}
-
+// up-projection's), then the normalized latent c_hat (mfa::qproj_layout).
 size_t mfa_qproj_workspace_size(int B, mfa_dtype dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(dt)) return 0;
-  return qproj_ws(B, dt, nullptr, nullptr, nullptr);
+  return mfa::qproj_layout(B, dt == MFA_BF16).total;
+}
+
+// The device's plans of the q path, checked against the reserved region
+// (a failed check would be a planning bug: it is reported, never run).
+static int qproj_plans(int B, bool bf, mfa::GemmPlan* dn, mfa::GemmPlan* up, mfa::QprojLayout* l) {
+  int st = MFA_OK;
+  const int cus = plan_cus(&st);
+  if (st != MFA_OK) return st;
+  *dn = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK, cus);
+  *up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus);
+  *l = mfa::qproj_layout(B, bf);
+  return mfa::qproj_part_need(B, bf, *dn, *up) <= l->part_bytes ? MFA_OK : MFA_ERR_WORKSPACE;
+}
+
+static int qproj_run(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps,
+                     const void* w_uq, const float* s_uq, void* q_out, void* ws, int B, bool bf, hipStream_t s) {
+  mfa::GemmPlan plan, up;
+  mfa::QprojLayout l;
+  const int st = qproj_plans(B, bf, &plan, &up, &l);
+  if (st != MFA_OK) return st;
+  float* part = (float*)ws;
+  void* chat = (char*)ws + l.chat_offset;
+  hipError_t e = mfa::launch_gemm(bf, plan, x, w_dq, w_dq, part, mfa::GemmOut::Partial, s, s_dq, s_dq);
+  if (e != hipSuccess) return hip_status(e);
+  e = mfa::launch_rmsnorm_reduce(bf, part, bf ? plan.splits : 1, B, MFA_RANK, gamma, eps, chat, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (bf && up.splits > 1) {
+    // the down-projection's partials were consumed by the reduce above
+    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s, s_uq, s_uq);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s));
+  }
+  return hip_status(mfa::launch_gemm(bf, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s, s_uq, s_uq));
 }
 
 int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq, void* q_out, void* ws,
@@ -118,30 +133,8 @@ int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, co
   if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(q_out) || !aligned16(ws) ||
       (gamma && !aligned_n(gamma, 4)))
     return MFA_ERR_ALIGNMENT;
-  // the documented size first (host only), then the device's own plan
-  if (!ws || ws_bytes < qproj_ws(B, dt, nullptr, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
-  mfa::GemmPlan plan, up;
-  int st = MFA_OK;
-  qproj_ws(B, dt, &plan, &up, &st);
-  if (st != MFA_OK) return st;
-  const bool bf = dt == MFA_BF16;
-  hipStream_t s = (hipStream_t)stream;
-  float* part = (float*)ws;
-  size_t part_bytes = bf ? mfa::gemm_partial_bytes(plan) : (size_t)B * MFA_RANK * sizeof(float);
-  if (bf && up.splits > 1 && mfa::gemm_partial_bytes(up) > part_bytes) part_bytes = mfa::gemm_partial_bytes(up);
-  void* chat = (char*)ws + align256(part_bytes);
-  hipError_t e = mfa::launch_gemm(bf, plan, x, w_dq, w_dq, part, mfa::GemmOut::Partial, s);
-  if (e != hipSuccess) return hip_status(e);
-  e = mfa::launch_rmsnorm_reduce(bf, part, bf ? plan.splits : 1, B, MFA_RANK, gamma, eps, chat, s);
-  if (e != hipSuccess) return hip_status(e);
-  if (bf && up.splits > 1) {
-    // the down-projection's partials were consumed by the reduce above
-    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s));
-  }
-  e = mfa::launch_gemm(bf, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s);
-  return hip_status(e);
+  if (!ws || ws_bytes < mfa_qproj_workspace_size(B, dt)) return MFA_ERR_WORKSPACE;
+  return qproj_run(x, w_dq, nullptr, gamma, eps, w_uq, nullptr, q_out, ws, B, dt == MFA_BF16, (hipStream_t)stream);
 }
 
 // Block-fp8 weights: the bf16 q path with e4m3 weight bytes and their
@@ -154,41 +147,23 @@ int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float
   if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(q_out) || !aligned16(ws) ||
       !aligned_n(s_dq, 4) || !aligned_n(s_uq, 4) || (gamma && !aligned_n(gamma, 4)))
     return MFA_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < qproj_ws(B, MFA_BF16, nullptr, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
-  mfa::GemmPlan plan, up;
-  int st = MFA_OK;
-  qproj_ws(B, MFA_BF16, &plan, &up, &st);
-  if (st != MFA_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  float* part = (float*)ws;
-  size_t part_bytes = mfa::gemm_partial_bytes(plan);
-  if (up.splits > 1 && mfa::gemm_partial_bytes(up) > part_bytes) part_bytes = mfa::gemm_partial_bytes(up);
-  void* chat = (char*)ws + align256(part_bytes);
-  hipError_t e = mfa::launch_gemm(true, plan, x, w_dq, w_dq, part, mfa::GemmOut::Partial, s, s_dq, s_dq);
-  if (e != hipSuccess) return hip_status(e);
-  e = mfa::launch_rmsnorm_reduce(true, part, plan.splits, B, MFA_RANK, gamma, eps, chat, s);
-  if (e != hipSuccess) return hip_status(e);
-  if (up.splits > 1) {
-    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s, s_uq, s_uq);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s));
-  }
-  return hip_status(mfa::launch_gemm(true, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s, s_uq, s_uq));
+  if (!ws || ws_bytes < mfa_qproj_workspace_size(B, MFA_BF16)) return MFA_ERR_WORKSPACE;
+  return qproj_run(x, w_dq, s_dq, gamma, eps, w_uq, s_uq, q_out, ws, B, true, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ K/V append
-static size_t kv_ws(int B, mfa_dtype act_dt, mfa::GemmPlan* plan_out, int* status) {
-  const bool bf = act_dt == MFA_BF16;
-  const int cus = plan_cus(status);
-  if (cus <= 0) return 0;
-  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM, cus);
-  if (plan_out) *plan_out = p;
-  return align256(bf ? mfa::gemm_partial_bytes(p) : (size_t)B * 2 * MFA_HEAD_DIM * sizeof(float));
-}
-
 size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(act_dt)) return 0;
-  return kv_ws(B, act_dt, nullptr, nullptr);
+  return mfa::kv_ws_bytes(B, act_dt == MFA_BF16);
+}
+
+// The device's plan of the [W_k; W_v] product, checked against the reserved region.
+static int kv_plan(int B, bool bf, mfa::GemmPlan* p) {
+  int st = MFA_OK;
+  const int cus = plan_cus(&st);
+  if (st != MFA_OK) return st;
+  *p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM, cus);
+  return mfa::kv_part_need(B, bf, *p) <= mfa::kv_ws_bytes(B, bf) ? MFA_OK : MFA_ERR_WORKSPACE;
 }
 
 int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache, void* v_cache,
@@ -202,12 +177,11 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
       !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) ||
       !aligned_n(seq_len_out, 4))
     return MFA_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < kv_ws(B, act_dt, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
-  mfa::GemmPlan plan;
-  int st = MFA_OK;
-  kv_ws(B, act_dt, &plan, &st);
-  if (st != MFA_OK) return st;
+  if (!ws || ws_bytes < mfa_kv_append_workspace_size(B, act_dt)) return MFA_ERR_WORKSPACE;
   const bool bf = act_dt == MFA_BF16;
+  mfa::GemmPlan plan;
+  const int st = kv_plan(B, bf, &plan);
+  if (st != MFA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
   if (e != hipSuccess) return hip_status(e);
@@ -232,12 +206,11 @@ int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_c
       !aligned16(ws) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) ||
       !aligned_n(seq_len_out, 4))
     return MFA_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < kv_ws(B, act_dt, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
-  mfa::GemmPlan plan;
-  int st = MFA_OK;
-  kv_ws(B, act_dt, &plan, &st);
-  if (st != MFA_OK) return st;
+  if (!ws || ws_bytes < mfa_kv_append_workspace_size(B, act_dt)) return MFA_ERR_WORKSPACE;
   const bool bf = act_dt == MFA_BF16;
+  mfa::GemmPlan plan;
+  const int st = kv_plan(B, bf, &plan);
+  if (st != MFA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
   if (e != hipSuccess) return hip_status(e);
@@ -263,10 +236,9 @@ int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const voi
       !aligned16(ws) || !aligned_n(s_k, 4) || !aligned_n(s_v, 4) || !aligned_n(seq_off, 8) || !aligned_n(seq_len, 4) ||
       !aligned_n(seq_len_out, 4))
     return MFA_ERR_ALIGNMENT;
-  if (!ws || ws_bytes < kv_ws(B, MFA_BF16, nullptr, nullptr)) return MFA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < mfa_kv_append_workspace_size(B, MFA_BF16)) return MFA_ERR_WORKSPACE;
   mfa::GemmPlan plan;
-  int st = MFA_OK;
-  kv_ws(B, MFA_BF16, &plan, &st);
+  const int st = kv_plan(B, true, &plan);
   if (st != MFA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(true, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s, s_k, s_v);
@@ -402,18 +374,24 @@ int mfa_decode_attn_paged_mt(const void* q, const void* k_pages, const void* v_p
 }
 
 // ------------------------------------------------------------------ out-projection
-static size_t oproj_ws(int B, mfa_dtype dt, mfa::GemmPlan* plan_out, int* status) {
-  const bool bf = dt == MFA_BF16;
-  const int cus = plan_cus(status);
-  if (cus <= 0) return 0;
-  const mfa::GemmPlan p = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN, cus);
-  if (plan_out) *plan_out = p;
-  return (bf && p.splits > 1) ? align256(mfa::gemm_partial_bytes(p)) : 0;
-}
-
 size_t mfa_oproj_workspace_size(int B, mfa_dtype dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(dt)) return 0;
-  return oproj_ws(B, dt, nullptr, nullptr);
+  return mfa::oproj_ws_bytes(B, dt == MFA_BF16);
+}
+
+static int oproj_run(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes, int B,
+                     bool bf, hipStream_t s) {
+  int st = MFA_OK;
+  const int cus = plan_cus(&st);
+  if (st != MFA_OK) return st;
+  const mfa::GemmPlan plan = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN, cus);
+  if (mfa::oproj_part_need(bf, plan) > ws_bytes) return MFA_ERR_WORKSPACE;  // within the documented size
+  if (bf && plan.splits > 1) {
+    hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s, s_o, s_o);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s));
+  }
+  return hip_status(mfa::launch_gemm(bf, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s, s_o, s_o));
 }
 
 int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_bytes, int B, mfa_dtype dt,
@@ -421,20 +399,9 @@ int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_by
   if (!attn || !w_o || !y || B < 1 || B > MFA_MAX_BATCH) return MFA_ERR_INVALID_ARG;
   if (!act_dtype_ok(dt)) return MFA_ERR_UNSUPPORTED;
   if (!aligned16(attn) || !aligned16(w_o) || !aligned16(y) || !aligned16(ws)) return MFA_ERR_ALIGNMENT;
-  const size_t need = oproj_ws(B, dt, nullptr, nullptr);
+  const size_t need = mfa_oproj_workspace_size(B, dt);
   if (need > 0 && (!ws || ws_bytes < need)) return MFA_ERR_WORKSPACE;
-  mfa::GemmPlan plan;
-  int st = MFA_OK;
-  oproj_ws(B, dt, &plan, &st);
-  if (st != MFA_OK) return st;
-  const bool bf = dt == MFA_BF16;
-  hipStream_t s = (hipStream_t)stream;
-  if (bf && plan.splits > 1) {
-    hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s));
-  }
-  return hip_status(mfa::launch_gemm(bf, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s));
+  return oproj_run(attn, w_o, nullptr, y, ws, ws ? ws_bytes : 0, B, dt == MFA_BF16, (hipStream_t)stream);
 }
 
 int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes, int B,
@@ -442,19 +409,9 @@ int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, v
   if (!attn || !w_o || !s_o || !y || B < 1 || B > MFA_MAX_BATCH) return MFA_ERR_INVALID_ARG;
   if (!aligned16(attn) || !aligned16(w_o) || !aligned16(y) || !aligned16(ws) || !aligned_n(s_o, 4))
     return MFA_ERR_ALIGNMENT;
-  const size_t need = oproj_ws(B, MFA_BF16, nullptr, nullptr);
+  const size_t need = mfa_oproj_workspace_size(B, MFA_BF16);
   if (need > 0 && (!ws || ws_bytes < need)) return MFA_ERR_WORKSPACE;
-  mfa::GemmPlan plan;
-  int st = MFA_OK;
-  oproj_ws(B, MFA_BF16, &plan, &st);
-  if (st != MFA_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (plan.splits > 1) {
-    hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s, s_o, s_o);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s));
-  }
-  return hip_status(mfa::launch_gemm(true, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s, s_o, s_o));
+  return oproj_run(attn, w_o, s_o, y, ws, ws ? ws_bytes : 0, B, true, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ bandwidth probe

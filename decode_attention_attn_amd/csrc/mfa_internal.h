@@ -8,6 +8,8 @@
 #include <tuple>
 #include <utility>
 
+#include "plan.h"
+
 namespace mfa {
 
 // Launch and return this launch's own status (not a stale error of earlier
@@ -72,17 +74,6 @@ enum class GemmOut {
   Direct    // final values [M][N] in the activation dtype
 };
 
-struct GemmPlan {
-  int M, N, K, N0;
-  int splits;   // S
-  int mchunks;  // ceil(M / 128) (bf16 path)
-  int tile_n;   // output columns per workgroup: 128 or 256 (bf16 path)
-};
-
-// bf16: MFMA kernel; f32: VALU kernel (no split).
-// cus: compute units of the device (the split-K factor fills them once).
-GemmPlan plan_gemm(bool bf16, int M, int N, int K, int N0, int cus);
-size_t gemm_partial_bytes(const GemmPlan& p);
 // S0 / S1 non-null: W0 / W1 are block-fp8 (e4m3 bytes, fp32 scales per 128 x 128 block, [rows/128][K/128])
 hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
                        GemmOut mode, hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr);

@@ -21,9 +21,9 @@
 
 namespace mfa {
 
-constexpr int kGN = 128;    // output columns (weight rows) per workgroup (narrow tile)
-constexpr int kGM = 128;    // batch rows per workgroup
-constexpr int kGK = 64;     // K per stage
+constexpr int kGN = kGemmTileN;  // output columns (weight rows) per workgroup (narrow tile)
+constexpr int kGM = kGemmTileM;  // batch rows per workgroup
+constexpr int kGK = kGemmChunkK; // K per stage
 
 // Tile shapes. Every wave owns 32 batch rows x 128 output columns. The wide
 // tile (8 waves, 256 columns) reads each activation chunk once per 256
@@ -404,41 +404,6 @@ __global__ __launch_bounds__(128) void kv_scatter_fp8_kernel(const float* part, 
 }
 
 // ------------------------------------------------------------------ host side
-GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) {
-  GemmPlan p{M, N, K, N0, 1, 1, kGN};
-  if (!bf16_path) return p;
-  p.mchunks = (M + kGM - 1) / kGM;
-  const int nch = K / kGK;
-  // For each tile width, split K so that the workgroups fill the compute
-  // units once (one per CU; a second partial wave would only lengthen the
-  // tail), then pick the width with the smaller estimated time: each CU
-  // streams (tile_n + 128) * K / S * 2 bytes of weights and activations, and
-  // the partial sums add 2 * S * M * N * 4 bytes across the chip.
-  double best = 0.0;
-  for (int tn = 128; tn <= 256; tn *= 2) {
-    if (N % tn != 0) continue;
-    const int tiles = (N / tn) * p.mchunks;
-    int s = cus / tiles;
-    // at least 4 K chunks per split: below that a workgroup is all start-up
-    // latency and the partial sums outgrow the weights
-    const int smax = nch / 4 > 0 ? nch / 4 : 1;
-    if (s > smax) s = smax;
-    if (s < 1) s = 1;
-    const int waves = (tiles * s + cus - 1) / cus;
-    const double per_cu = (double)(tn + kGM) * K / s * 2.0 * waves;  // bytes, ~30 GB/s per CU
-    const double partial = s > 1 ? 2.0 * s * M * (double)N * 4.0 : 0.0;  // bytes, ~5 TB/s chip-wide
-    const double t = per_cu / 30e9 + partial / 5e12;
-    if (best == 0.0 || t < best) {
-      best = t;
-      p.tile_n = tn;
-      p.splits = s;
-    }
-  }
-  return p;
-}
-
-size_t gemm_partial_bytes(const GemmPlan& p) { return (size_t)p.splits * p.M * p.N * sizeof(float); }
-
 hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
                        GemmOut mode, hipStream_t stream, const float* S0, const float* S1) {
   if (!bf16_path) {

@@ -1,0 +1,50 @@
+// Host-only check of the projection workspace sizing: for every batch size
+// in a sweep and every compute-unit count 1..256, the plan a device would
+// make must fit the region a workspace query reserves without a device.
+// Prints one line per violation and exits non-zero if there is any.
+#include <stdio.h>
+
+#include "plan.h"
+
+int main() {
+  using namespace mfa;
+  long bad = 0, checked = 0;
+  int batches[600];
+  int nb = 0;
+  for (int b = 1; b <= 300; ++b) batches[nb++] = b;
+  for (int b = 301; b <= 65536 && nb < 600; b = b * 5 / 4 + 1) batches[nb++] = b;
+  for (int i = 0; i < nb; ++i) {
+    const int B = batches[i];
+    for (int bf = 0; bf < 2; ++bf) {
+      const QprojLayout ql = qproj_layout(B, bf);
+      const size_t kv = kv_ws_bytes(B, bf);
+      const size_t op = oproj_ws_bytes(B, bf);
+      if (ql.chat_offset < ql.part_bytes || ql.total < ql.chat_offset + (size_t)B * kPlanRank * (bf ? 2 : 4)) {
+        printf("q layout overlaps: B=%d bf=%d\n", B, bf);
+        ++bad;
+      }
+      for (int cus = 1; cus <= kPlanCus; ++cus) {
+        const GemmPlan dn = plan_gemm(bf, B, kPlanRank, kPlanHidden, kPlanRank, cus);
+        const GemmPlan up = plan_gemm(bf, B, kPlanQDim, kPlanRank, kPlanQDim, cus);
+        const GemmPlan kp = plan_gemm(bf, B, 2 * kPlanHeadDim, kPlanHidden, kPlanHeadDim, cus);
+        const GemmPlan opl = plan_gemm(bf, B, kPlanHidden, kPlanQDim, kPlanHidden, cus);
+        const size_t q_need = qproj_part_need(B, bf, dn, up);
+        if (q_need > ql.part_bytes) {
+          printf("q path: B=%d bf=%d cus=%d needs %zu > %zu\n", B, bf, cus, q_need, ql.part_bytes);
+          ++bad;
+        }
+        if (kv_part_need(B, bf, kp) > kv) {
+          printf("kv: B=%d bf=%d cus=%d needs %zu > %zu\n", B, bf, cus, kv_part_need(B, bf, kp), kv);
+          ++bad;
+        }
+        if (oproj_part_need(bf, opl) > op) {
+          printf("oproj: B=%d bf=%d cus=%d needs %zu > %zu\n", B, bf, cus, oproj_part_need(bf, opl), op);
+          ++bad;
+        }
+        checked += 3;
+      }
+    }
+  }
+  printf("checked %ld plans, %ld over their workspace\n", checked, bad);
+  return bad == 0 ? 0 : 1;
+}
