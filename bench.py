@@ -76,41 +76,86 @@ def _kv_bytes(lengths, kv_kind):
 _SPREAD = {}  # per-call time percentiles of the last graph-timed run (ms)
 
 
-def _event_time_ms(fn, steps, warmup, stream, graph_calls=0):
-    """Average time per step between HIP events on ``stream``.
+def graph_plan(steps, rotate, max_calls=16):
+    """How ``steps`` calls are replayed: (calls per graph, replays, remainder).
 
-    With ``graph_calls`` > 0 the steps are captured ``graph_calls`` at a time
-    into a HIP graph (through torch's graph capture, which records the
-    library's launches on the capture stream) and the graph is replayed, so
-    host-side launch latency does not show in the device time, as in a serving
-    loop. ``fn(i)`` must only enqueue work on the current stream.
+    The main graph holds a multiple of ``rotate`` calls (so consecutive calls
+    always use different K/V buffer sets) and is replayed ``replays`` times;
+    ``remainder`` calls (fewer than ``rotate``) follow in a second graph
+    replayed once. The largest graph that still gives at least 5 replays is
+    preferred; calls timed = calls * replays + remainder = steps, exactly."""
+    best = None
+    for c in range(rotate, max_calls + 1, rotate):
+        if steps % c == 0 and steps // c >= 5:
+            best = c
+    if best is not None:
+        return best, steps // best, 0
+    c = rotate if steps >= rotate else 0
+    return (c, steps // c, steps % c) if c else (0, 0, steps)
+
+
+def _event_time_ms(fn, steps, warmup, stream, rotate=1):
+    """Average time per step between HIP events on ``stream`` over exactly
+    ``steps`` steps after ``warmup`` untimed ones.
+
+    The steps are captured into HIP graphs (through torch's graph capture,
+    which records the library's launches on the capture stream) and the graphs
+    are replayed (``graph_plan``), so host-side launch latency does not show
+    in the device time, as in a serving loop. An event after every replay of
+    the main graph gives the per-call time of each replay; their 10th, 50th
+    and 90th percentiles are kept when there are at least 5 replays.
+    ``fn(i)`` must only enqueue work on the current stream; step i uses
+    buffer set i % rotate.
     """
+    import torch
+
+    _SPREAD.clear()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    calls, reps, rem = graph_plan(steps, rotate)
+    graphs = []
+    for n, r in ((calls, reps), (rem, 1 if rem else 0)):
+        if n == 0 or r == 0:
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+        graphs.append((g, n, r))
+    torch.cuda.synchronize()
+    for g, _, _ in graphs:  # one untimed replay of each graph
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True)]
+    ev[0].record(stream)
+    marks = []  # calls in each timed replay, main graph first
+    for g, n, r in graphs:
+        for _ in range(r):
+            g.replay()
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev.append(e)
+            marks.append(n)
+    torch.cuda.synchronize()
+    timed = sum(marks)
+    assert timed == steps, (timed, steps)
+    main = [ev[k].elapsed_time(ev[k + 1]) / marks[k] for k in range(reps)] if calls else []
+    if len(main) >= 5:
+        per = sorted(main)
+        _SPREAD.update(p10=per[int(0.1 * (len(per) - 1))], p50=per[(len(per) - 1) // 2],
+                       p90=per[int(0.9 * (len(per) - 1))], replays=len(per), calls_per_replay=calls)
+    return ev[0].elapsed_time(ev[-1]) / steps
+
+
+def _eager_time_ms(fn, steps, warmup, stream):
+    """Average time per step between HIP events on ``stream``, every step
+    launched from the host (no graph)."""
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    if graph_calls > 0:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(graph_calls):
-                fn(i)
-        torch.cuda.synchronize()
-        reps = max(1, steps // graph_calls)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        # one event between replays: the mean over all of them, and the
-        # spread of per-call times replay by replay
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        ev[0].record(stream)
-        for r in range(reps):
-            g.replay()
-            ev[r + 1].record(stream)
-        torch.cuda.synchronize()
-        per = sorted(ev[r].elapsed_time(ev[r + 1]) / graph_calls for r in range(reps))
-        _SPREAD.update(p10=per[int(0.1 * (reps - 1))], p50=per[(reps - 1) // 2], p90=per[int(0.9 * (reps - 1))])
-        return ev[0].elapsed_time(ev[reps]) / (reps * graph_calls)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -141,8 +186,8 @@ def bench_attn(name, steps, warmup, rotate, graph=True):
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         call = runner.AttnCall(dev, num_workgroups=0, want_lse=False, stream=None)
-        ms = _event_time_ms(lambda i: call(ks[i % rotate], vs[i % rotate]), steps, warmup, stream,
-                            graph_calls=4 * rotate if graph else 0)
+        ms = (_event_time_ms(lambda i: call(ks[i % rotate], vs[i % rotate]), steps, warmup, stream, rotate)
+              if graph else _eager_time_ms(lambda i: call(ks[i % rotate], vs[i % rotate]), steps, warmup, stream))
     B = w.batch
     kv = _kv_bytes(inp["seq_len"], w.kv)
     qo = 2 * nt * B * 64 * 256 * (4 if w.act == "f32" else 2)
@@ -163,7 +208,8 @@ def bench_layer(name, steps, warmup, graph=True):
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         call = runner.LayerCall(dev, num_workgroups=0, stream=None)
-        ms = _event_time_ms(lambda i: call(), steps, warmup, stream, graph_calls=8 if graph else 0)
+        ms = (_event_time_ms(lambda i: call(), steps, warmup, stream) if graph
+              else _eager_time_ms(lambda i: call(), steps, warmup, stream))
     B = w.batch
     esz = 4 if w.act == "f32" else 2
     kv = _kv_bytes(inp["seq_len"] + 1, w.kv)
@@ -186,7 +232,7 @@ def bench_probe(gib=4, reps=10):
     buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(cus, dtype=torch.int32, device="cuda")
-    ms = _event_time_ms(lambda i: mfa.check(mfa.mfa_bw_probe(buf, sink), "mfa_bw_probe"), reps, 2,
+    ms = _eager_time_ms(lambda i: mfa.check(mfa.mfa_bw_probe(buf, sink), "mfa_bw_probe"), reps, 2,
                         torch.cuda.current_stream())
     out = {"GBps": round(buf.numel() / (ms * 1e-3) / 1e9, 1), "bytes": buf.numel(), "ms": round(ms, 4),
            "kernel": "mfa_bw_probe (nontemporal 16-byte vector loads, one workgroup per CU)"}
@@ -207,6 +253,16 @@ def cpu_baseline(res, seconds):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    host_cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     inp, w = res["inp"], res["w"]
     B = len(inp["seq_len"])
     done_seqs, done_kv, t0 = 0, 0, time.perf_counter()
@@ -233,7 +289,9 @@ def cpu_baseline(res, seconds):
         "value": round(done_kv / dt / 1e9, 4),
         "unit": "GB/s",
         "tokens_per_s": round(done_seqs / dt, 3),
-        "cores": int(threads),
+        "cores": int(threads),  # BLAS threads the oracle ran with
+        "host_cores": host_cores,  # cores this process may run on
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{done_seqs} sequences of {w.name} (cycling over the batch), {dt:.1f} s, numpy float64",
         "seconds": round(dt, 2),
@@ -298,7 +356,7 @@ def main():
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": args.steps,  # calls timed, exactly
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -318,8 +376,10 @@ def main():
             "kv_buffer_sets": args.rotate if w.kind == "attn" else 1,
         },
         "tokens_per_s": round(res.get("tokens", w.batch) / (ms * 1e-3), 1),
-        # per-call time over each graph replay: 10th, 50th and 90th percentiles (ms)
-        "ms_per_step_pct": {k: round(v, 5) for k, v in res.get("spread", {}).items()} or None,
+        # per-call time over each graph replay: 10th, 50th and 90th percentiles (ms), given when the
+        # timed calls form at least 5 replays
+        "ms_per_step_pct": {k: (round(v, 5) if isinstance(v, float) else v)
+                            for k, v in res.get("spread", {}).items()} or None,
         "pct_of_peak_hbm": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",

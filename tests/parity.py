@@ -33,14 +33,15 @@ def passes(got, ref, atol, rel):
     return float(np.max(np.abs(got - ref))) <= atol and rel_l2(got, ref) <= rel
 
 
-def check(name, got, ref, atol, rel):
+def check(name, got, ref, atol, rel, quiet=False):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values in GPU output"
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
     r = rel_l2(got, ref)
-    print(f"[parity] {name}: max_abs={err:.3e} (tol {atol:g}) rel_l2={r:.3e} (tol {rel:g})", flush=True)
+    if not quiet or err > atol or r > rel:
+        print(f"[parity] {name}: max_abs={err:.3e} (tol {atol:g}) rel_l2={r:.3e} (tol {rel:g})", flush=True)
     assert err <= atol, f"{name}: max abs error {err:.3e} > {atol}"
     assert r <= rel, f"{name}: relative L2 error {r:.3e} > {rel}"
 

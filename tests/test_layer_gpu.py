@@ -35,46 +35,55 @@ def _run_layer(inp, num_workgroups=0):
     return runner, dev, call, k_before, v_before
 
 
-def _check_layer(inp, ids, kind, num_workgroups=0):
+def _stage_isolated_attn(runner, dev, call, inp, ids, chunk=16):
+    """Oracle attention fed the GPU's own q and cache rows (sequences ``ids``,
+    ``chunk`` at a time, so only that many sequences' rows sit on the host)."""
+    outs, lses = [], []
+    for c0 in range(0, len(ids), chunk):
+        part = list(ids[c0:c0 + chunk])
+        lens = inp["seq_len"][part] + 1
+        sel = torch.cat([torch.arange(int(inp["seq_off"][b]), int(inp["seq_off"][b]) + int(n),
+                                      device=dev["k"].device) for b, n in zip(part, lens)])
+        offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+        o, lse = om.decode_attn(runner.to_f64(call.q[torch.as_tensor(part, device=call.q.device)]),
+                                runner.to_f64(dev["k"][sel]), runner.to_f64(dev["v"][sel]), offs, lens)
+        outs.append(o)
+        lses.append(lse)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+def _check_layer(inp, kind, ids=None, num_workgroups=0):
+    """Every output of the sequences ``ids`` (all of them by default)."""
     runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups)
     # the append hands attention the length including the new row
     assert torch.equal(call.len_after, dev["len"] + 1)
     t = TOL[kind]
-    ref = om.decode_layer(inp, batch_ids=ids)
     B = len(inp["seq_len"])
+    ids = list(range(B)) if ids is None else list(ids)
+    ref = om.decode_layer(inp, batch_ids=ids)
     rows = (inp["seq_off"] + inp["seq_len"]).astype(np.int64)
-    # q and the appended rows, for every sequence
-    ref_all = om.decode_layer(inp, batch_ids=list(range(B))) if B <= 8 else None
-    if ref_all is not None:
-        q_ref, k_ref, v_ref = ref_all["q"], ref_all["k_new"], ref_all["v_new"]
-        q_ids = list(range(B))
-    else:
-        q_ref, k_ref, v_ref, q_ids = ref["q"], ref["k_new"], ref["v_new"], ids
-    check(f"{kind} q", runner.to_f64(call.q)[q_ids], q_ref, t["atol"], t["rel"])
-    k_new = runner.to_f64(dev["k"][torch.as_tensor(rows[q_ids], device=dev["k"].device)])
-    v_new = runner.to_f64(dev["v"][torch.as_tensor(rows[q_ids], device=dev["v"].device)])
-    check(f"{kind} k_new", k_new, k_ref, t["atol"], t["rel"])
-    check(f"{kind} v_new", v_new, v_ref, t["atol"], t["rel"])
+    check(f"{kind} q", runner.to_f64(call.q)[ids], ref["q"], t["atol"], t["rel"])
+    k_new = runner.to_f64(dev["k"][torch.as_tensor(rows[ids], device=dev["k"].device)])
+    v_new = runner.to_f64(dev["v"][torch.as_tensor(rows[ids], device=dev["v"].device)])
+    check(f"{kind} k_new", k_new, ref["k_new"], t["atol"], t["rel"])
+    check(f"{kind} v_new", v_new, ref["v_new"], t["atol"], t["rel"])
     # no other cache row changed
     mask = torch.ones(dev["k"].shape[0], dtype=torch.bool, device=dev["k"].device)
     mask[torch.as_tensor(rows, device=mask.device)] = False
     assert torch.equal(dev["k"][mask], k_before[mask]) and torch.equal(dev["v"][mask], v_before[mask])
     # attention and output, end to end
-    check(f"{kind} o (end to end)", runner.to_f64(call.o)[ids], ref["o"], t["atol"], t["rel"])
+    o_got = runner.to_f64(call.o)[ids]
+    check(f"{kind} o (end to end, {len(ids)} sequences)", o_got, ref["o"], t["atol"], t["rel"])
+    for i, b in enumerate(ids):
+        check(f"{kind} o[{b}] (end to end)", o_got[i], ref["o"][i], t["atol"], t["rel"], quiet=True)
     check_lse(f"{kind} lse (end to end)", runner.to_f64(call.lse)[ids], ref["lse"], max(t["lse"], 5e-3))
     check(f"{kind} y (end to end)", runner.to_f64(call.y)[ids], ref["y"], t["atol"], t["rel"])
     # stage isolated: oracle attention on the GPU's q and cache, oracle y on the GPU's o
-    qg = runner.to_f64(call.q)[ids]
-    lens = inp["seq_len"][ids] + 1
-    spans = [torch.arange(int(inp["seq_off"][b]), int(inp["seq_off"][b]) + int(n), device=dev["k"].device)
-             for b, n in zip(ids, lens)]
-    sel = torch.cat(spans)
-    kc, vc = runner.to_f64(dev["k"][sel]), runner.to_f64(dev["v"][sel])
-    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
-    o_iso, l_iso = om.decode_attn(qg, kc, vc, offs, lens)
-    check(f"{kind} o (stage isolated)", runner.to_f64(call.o)[ids], o_iso, t["atol"], t["rel"])
-    y_iso = om.out_proj(runner.to_f64(call.o)[ids], _w_o(inp))
+    o_iso, _ = _stage_isolated_attn(runner, dev, call, inp, ids)
+    check(f"{kind} o (stage isolated)", o_got, o_iso, t["atol"], t["rel"])
+    y_iso = om.out_proj(o_got, _w_o(inp))
     check(f"{kind} y (stage isolated)", runner.to_f64(call.y)[ids], y_iso, t["atol"], t["rel"])
+    return runner, dev, call, ref
 
 
 def _w_o(inp):
@@ -86,7 +95,7 @@ def _w_o(inp):
 def test_layer_tiny_fp32_full():
     print("[case] layer tiny_fp32 (full size)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["tiny_fp32"])
-    _check_layer(inp, [0, 1], "f32")
+    _check_layer(inp, "f32")
 
 
 @pytest.mark.parametrize("G", [0, 3])
@@ -94,7 +103,7 @@ def test_layer_bf16_small(G):
     print(f"[case] layer bf16 small B=5 ctx=300 G={G}", flush=True)
     w = gen.scaled(gen.WORKLOADS["layer_bf16_8k"], batch=5, ctx=300)
     inp = gen.make_layer(w)
-    _check_layer(inp, [0, 2, 4], "bf16", num_workgroups=G)
+    _check_layer(inp, "bf16", num_workgroups=G)
 
 
 @pytest.mark.parametrize("B", [1, 200])
@@ -104,8 +113,7 @@ def test_layer_bf16_batch_edges(B):
     print(f"[case] layer bf16 B={B} ctx=64", flush=True)
     w = gen.scaled(gen.WORKLOADS["layer_bf16_8k"], batch=B, ctx=64)
     inp = gen.make_layer(w)
-    ids = [0] if B == 1 else [0, 127, 128, 199]
-    _check_layer(inp, ids, "bf16")
+    _check_layer(inp, "bf16")
 
 
 def test_layer_maximum_batch():
@@ -145,9 +153,9 @@ def test_layer_maximum_batch():
 
 
 def test_layer_bf16_8k_full():
-    print("[case] layer layer_bf16_8k (full size, sampled sequences)", flush=True)
+    print("[case] layer layer_bf16_8k (full size, every sequence)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_bf16_8k"])
-    _check_layer(inp, [0, 77, 127], "bf16")
+    _check_layer(inp, "bf16")
 
 
 # ------------------------------------------------------------------ e4m3 cache (quantize on append)
@@ -169,9 +177,10 @@ def _check_codes(name, got, want, exact, scale):
     assert same.mean() >= 0.99, f"{name}: only {same.mean():.4f} of the codes agree"
 
 
-def _check_layer_fp8(inp, ids, num_workgroups=0):
+def _check_layer_fp8(inp, ids=None, num_workgroups=0):
     runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups)
     t, tb = TOL["fp8_e4m3"], TOL["bf16"]
+    ids = list(range(len(inp["seq_len"]))) if ids is None else list(ids)
     ref = om.decode_layer(inp, batch_ids=ids)
     rows = (inp["seq_off"] + inp["seq_len"]).astype(np.int64)
     sel = torch.as_tensor(rows[ids], device=dev["k"].device)
@@ -182,7 +191,10 @@ def _check_layer_fp8(inp, ids, num_workgroups=0):
     mask = torch.ones(dev["k"].shape[0], dtype=torch.bool, device=dev["k"].device)
     mask[torch.as_tensor(rows, device=mask.device)] = False
     assert torch.equal(dev["k"][mask], k_before[mask]) and torch.equal(dev["v"][mask], v_before[mask])
-    check("fp8 layer o (end to end)", runner.to_f64(call.o)[ids], ref["o"], t["atol"], t["rel"])
+    o_got = runner.to_f64(call.o)[ids]
+    check(f"fp8 layer o (end to end, {len(ids)} sequences)", o_got, ref["o"], t["atol"], t["rel"])
+    for i, b in enumerate(ids):
+        check(f"fp8 layer o[{b}] (end to end)", o_got[i], ref["o"][i], t["atol"], t["rel"], quiet=True)
     check_lse("fp8 layer lse (end to end)", runner.to_f64(call.lse)[ids], ref["lse"], max(t["lse"], 5e-3))
     check("fp8 layer y (end to end)", runner.to_f64(call.y)[ids], ref["y"], t["atol"], t["rel"])
 
@@ -191,13 +203,13 @@ def _check_layer_fp8(inp, ids, num_workgroups=0):
 def test_layer_fp8_cache_small(G):
     print(f"[case] layer bf16 with e4m3 cache B=5 ctx=300 G={G}", flush=True)
     w = gen.scaled(gen.WORKLOADS["layer_bf16_fp8kv_8k"], batch=5, ctx=300)
-    _check_layer_fp8(gen.make_layer(w), [0, 1, 2, 3, 4], num_workgroups=G)
+    _check_layer_fp8(gen.make_layer(w), num_workgroups=G)
 
 
 def test_layer_fp8_cache_full():
-    print("[case] layer layer_bf16_fp8kv_8k (full size, sampled sequences)", flush=True)
+    print("[case] layer layer_bf16_fp8kv_8k (full size, every sequence)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_bf16_fp8kv_8k"])
-    _check_layer_fp8(inp, [0, 64, 127])
+    _check_layer_fp8(inp)
 
 
 # ------------------------------------------------------------------ block-fp8 weights
@@ -207,22 +219,22 @@ def test_layer_block_fp8_weights_small(kv):
     w = dataclasses.replace(gen.scaled(gen.WORKLOADS["layer_fp8_8k"], batch=5, ctx=300), kv=kv)
     inp = gen.make_layer(w)
     if kv == gen.FP8:
-        _check_layer_fp8(inp, [0, 1, 2, 3, 4])
+        _check_layer_fp8(inp)
     else:
-        _check_layer(inp, [0, 2, 4], "bf16")
+        _check_layer(inp, "bf16")
 
 
 def test_layer_block_fp8_weights_batch_200():
     # a second, partly filled 128-row batch chunk in every block-fp8 projection
     print("[case] layer block-fp8 weights, bf16 cache, B=200 ctx=64", flush=True)
     w = dataclasses.replace(gen.scaled(gen.WORKLOADS["layer_fp8_8k"], batch=200, ctx=64), kv=gen.BF16)
-    _check_layer(gen.make_layer(w), [0, 127, 128, 199], "bf16")
+    _check_layer(gen.make_layer(w), "bf16")
 
 
 def test_layer_block_fp8_full():
-    print("[case] layer layer_fp8_8k (full size, sampled sequences)", flush=True)
+    print("[case] layer layer_fp8_8k (full size, every sequence)", flush=True)
     inp = gen.make_layer(gen.WORKLOADS["layer_fp8_8k"])
-    _check_layer_fp8(inp, [0, 64, 127])
+    _check_layer_fp8(inp)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
@@ -294,22 +306,41 @@ def test_kv_append_fp8_f32_activations_and_saturation():
     assert np.array_equal(gk[keep], kc[keep]) and np.array_equal(gv[keep], vc[keep])
 
 
-def test_layer_step_replays_from_a_hip_graph():
+def _check_replay_against_oracle(runner, dev, call, inp, ref, rep):
+    t = TOL["bf16"]
+    rows = torch.as_tensor((inp["seq_off"] + inp["seq_len"]).astype(np.int64), device=dev["k"].device)
+    check(f"replay {rep} q", runner.to_f64(call.q), ref["q"], t["atol"], t["rel"])
+    check(f"replay {rep} k_new", runner.to_f64(dev["k"][rows]), ref["k_new"], t["atol"], t["rel"])
+    check(f"replay {rep} v_new", runner.to_f64(dev["v"][rows]), ref["v_new"], t["atol"], t["rel"])
+    o = runner.to_f64(call.o)
+    check(f"replay {rep} o", o, ref["o"], t["atol"], t["rel"])
+    for b in range(len(o)):
+        check(f"replay {rep} o[{b}]", o[b], ref["o"][b], t["atol"], t["rel"], quiet=True)
+    check_lse(f"replay {rep} lse", runner.to_f64(call.lse), ref["lse"], max(t["lse"], 5e-3))
+    check(f"replay {rep} y", runner.to_f64(call.y), ref["y"], t["atol"], t["rel"])
+
+
+@pytest.mark.parametrize("name,batch,ctx,reps", [("small", 5, 300, 3), ("layer_bf16_8k", None, None, 2)])
+def test_layer_step_replays_from_a_hip_graph(name, batch, ctx, reps):
     # The four calls allocate nothing and never wait on the host, so a whole
     # step captures into one HIP graph; every replay (with eager work that
-    # clobbers the outputs in between) must equal the eager step bitwise.
-    print("[case] layer bf16 B=5 ctx=300 captured in a HIP graph, 3 replays", flush=True)
-    w = gen.scaled(gen.WORKLOADS["layer_bf16_8k"], batch=5, ctx=300)
+    # clobbers the outputs and restores the cache in between) must equal the
+    # eager step bitwise and match the oracle's step on every sequence.
+    w = gen.WORKLOADS["layer_bf16_8k"]
+    if batch is not None:
+        w = gen.scaled(w, batch=batch, ctx=ctx)
+    print(f"[case] layer bf16 {name} (B={w.batch}) captured in a HIP graph, {reps} replays", flush=True)
     inp = gen.make_layer(w)
     runner, dev, call, k_before, v_before = _run_layer(inp)
     want = [t.clone() for t in (call.q, call.o, call.lse, call.y, dev["k"], dev["v"])]
+    ref = om.decode_layer(inp)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(g, stream=side):
         call()
     torch.cuda.synchronize()
-    for rep in range(3):
+    for rep in range(reps):
         for t in (call.q, call.o, call.lse, call.y):
             t.fill_(float(rep + 7))
         dev["k"].copy_(k_before)
@@ -318,5 +349,6 @@ def test_layer_step_replays_from_a_hip_graph():
         g.replay()
         torch.cuda.synchronize()
         got = (call.q, call.o, call.lse, call.y, dev["k"], dev["v"])
-        for name, a, b in zip(("q", "o", "lse", "y", "k", "v"), got, want):
-            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
+        for nm, a, b in zip(("q", "o", "lse", "y", "k", "v"), got, want):
+            assert torch.equal(a, b), f"replay {rep}: {nm} differs from the eager step"
+        _check_replay_against_oracle(runner, dev, call, inp, ref, rep)
