@@ -41,6 +41,8 @@
 //    a score exceeds it by more than 8 (a factor 256), so the O accumulator is
 //    rescaled on a piece's first tile and rarely after; row sums are combined
 //    across the 4 lanes of a head with the gfx950 row swaps at piece end.
+#include <atomic>
+
 #include "mfa_common.h"
 #include "mfa_internal.h"
 
@@ -992,6 +994,33 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
       break;
   }
   return e;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: partial outputs, their lse and
+// the merge records, laid out as in a caller's workspace. The runtime places
+// one copy on every GPU that loads this code object. On the host `scratch`
+// only stands for the symbol and is never passed to a kernel or a copy: host
+// code uses the device address hipGetSymbolAddress returns for the current
+// device, looked up on the first call on that device and kept.
+static __device__ __align__(256) char scratch[kAttnScratchBytes];
+
+hipError_t attn_scratch(void** ptr) {
+  constexpr int kDevices = 64;
+  static std::atomic<void*> addr[kDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace mfa

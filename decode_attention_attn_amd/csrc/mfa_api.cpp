@@ -263,11 +263,12 @@ size_t mfa_decode_attn_workspace_size(int B, int num_workgroups) {
 }
 
 // Shared by the contiguous and the paged entry points (table == null: contiguous).
+// use_scratch: the library's own static scratch replaces ws / ws_bytes.
 static int decode_attn_impl(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
                             const int32_t* block_table, int max_blocks, int page_rows, const int32_t* seq_len,
                             int n_tokens, float softmax_scale, float k_scale, float v_scale, void* out, float* lse,
                             void* ws, size_t ws_bytes, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt,
-                            void* stream) {
+                            void* stream, bool use_scratch = false) {
   const bool paged = block_table != nullptr;
   if (!q || !k_cache || !v_cache || (!paged && !seq_off) || !seq_len || !out || B < 1 || B > MFA_MAX_BATCH ||
       num_workgroups < 0 || num_workgroups > 65536 || !isfinite(softmax_scale) || !isfinite(k_scale) ||
@@ -288,11 +289,16 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
     kind = mfa::AttnKind::BF16_FP8KV;
   else
     return MFA_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws) ||
-      (!paged && !aligned_n(seq_off, 8)) || (paged && !aligned_n(block_table, 4)) || !aligned_n(seq_len, 4) ||
-      (lse && !aligned_n(lse, 4)))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (!use_scratch && !aligned16(ws)) || (!paged && !aligned_n(seq_off, 8)) ||
+      (paged && !aligned_n(block_table, 4)) || !aligned_n(seq_len, 4) || (lse && !aligned_n(lse, 4)))
     return MFA_ERR_ALIGNMENT;
-  if (!ws) return MFA_ERR_WORKSPACE;
+  if (use_scratch) {
+    ws = nullptr;
+    ws_bytes = mfa::kAttnScratchBytes;
+  } else if (!ws) {
+    return MFA_ERR_WORKSPACE;
+  }
   int G = num_workgroups;
   if (G == 0) {
     int st = MFA_OK;
@@ -300,6 +306,10 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
     if (st != MFA_OK) return st;
   }
   if (ws_bytes < mfa::attn_ws_bytes(B, G, n_tokens)) return MFA_ERR_WORKSPACE;
+  if (use_scratch) {
+    const hipError_t e = mfa::attn_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
   mfa::AttnLaunch p;
   p.kind = kind;
   p.q = q;
@@ -329,6 +339,16 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
   if (!seq_off) return MFA_ERR_INVALID_ARG;
   return decode_attn_impl(q, k_cache, v_cache, seq_off, nullptr, 0, 0, seq_len, 1, softmax_scale, k_scale, v_scale,
                           out, lse, ws, ws_bytes, B, num_workgroups, q_dt, kv_dt, stream);
+}
+
+static_assert(MFA_NOALLOC_SCRATCH_BYTES == mfa::kAttnScratchBytes, "scratch size in the header");
+
+int mfa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                            const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale, void* out,
+                            float* lse, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream) {
+  if (!seq_off) return MFA_ERR_INVALID_ARG;
+  return decode_attn_impl(q, k_cache, v_cache, seq_off, nullptr, 0, 0, seq_len, 1, softmax_scale, k_scale, v_scale,
+                          out, lse, nullptr, 0, B, num_workgroups, q_dt, kv_dt, stream, true);
 }
 
 size_t mfa_decode_attn_mt_workspace_size(int B, int n_tokens, int num_workgroups) {

@@ -63,6 +63,12 @@ inline size_t attn_ws_bytes(int B, int G, int nt = 1) { return attn_meta_offset(
 
 hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream);
 
+// Library-owned device scratch of the allocation-free attention call (one
+// copy per GPU, held until the process ends): its size, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kAttnScratchBytes = (size_t)40 << 20;
+hipError_t attn_scratch(void** ptr);
+
 // Streaming-read probe: G workgroups XOR bytes / 16 16-byte words of buf,
 // one 32-bit checksum per workgroup into sink[G].
 hipError_t launch_bw_probe(const void* buf, size_t bytes, unsigned* sink, int G, hipStream_t stream);

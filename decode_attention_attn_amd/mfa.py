@@ -61,6 +61,8 @@ _lib.mfa_decode_attn_workspace_size.restype = _Z
 _lib.mfa_decode_attn_workspace_size.argtypes = [_I, _I]
 _lib.mfa_decode_attn.restype = _I
 _lib.mfa_decode_attn.argtypes = [_P, _P, _P, _P, _P, _F, _F, _F, _P, _P, _P, _Z, _I, _I, _I, _I, _P]
+_lib.mfa_decode_attn_noalloc.restype = _I
+_lib.mfa_decode_attn_noalloc.argtypes = [_P, _P, _P, _P, _P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _P]
 _lib.mfa_decode_attn_mt_workspace_size.restype = _Z
 _lib.mfa_decode_attn_mt_workspace_size.argtypes = [_I, _I, _I]
 _lib.mfa_decode_attn_mt.restype = _I
@@ -87,7 +89,8 @@ EXPORTED = [
     "mfa_version", "mfa_status_string", "mfa_last_hip_error",
     "mfa_qproj_workspace_size", "mfa_qproj",
     "mfa_kv_append_workspace_size", "mfa_kv_append", "mfa_kv_append_fp8",
-    "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_paged", "mfa_decode_attn_paged_mt",
+    "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_noalloc", "mfa_decode_attn_paged",
+    "mfa_decode_attn_paged_mt",
     "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
     "mfa_oproj_workspace_size", "mfa_oproj",
     "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8", "mfa_bw_probe",
@@ -178,6 +181,16 @@ def mfa_decode_attn(q, k_cache, v_cache, seq_off, seq_len, softmax_scale, k_scal
     return _lib.mfa_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off), _ptr(seq_len),
                                 softmax_scale, k_scale, v_scale, _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), B,
                                 num_workgroups, q_dt, kv_dt, _stream(stream))
+
+
+MFA_NOALLOC_SCRATCH_BYTES = 40 << 20
+
+
+def mfa_decode_attn_noalloc(q, k_cache, v_cache, seq_off, seq_len, softmax_scale, k_scale, v_scale, out, lse, B,
+                            num_workgroups, q_dt, kv_dt, stream=None) -> int:
+    return _lib.mfa_decode_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off), _ptr(seq_len),
+                                        softmax_scale, k_scale, v_scale, _ptr(out), _ptr(lse), B, num_workgroups,
+                                        q_dt, kv_dt, _stream(stream))
 
 
 def mfa_decode_attn_mt_workspace_size(B: int, n_tokens: int, num_workgroups: int = 0) -> int:

@@ -29,8 +29,10 @@
  *    size) run on the host before any HIP call. A failed launch returns
  *    MFA_ERR_HIP. Device-side preconditions (documented per call) are not
  *    checked.
- *  - Calls on different streams or threads are independent; the library keeps
- *    no state besides a cached per-device property table.
+ *  - Calls on different streams or threads are independent, except calls of
+ *    mfa_decode_attn_noalloc on one GPU, which share that GPU's library-owned
+ *    scratch buffer; the library keeps no other state than a cached
+ *    per-device property table and that buffer's per-device address.
  */
 #ifndef MFA_H_
 #define MFA_H_
@@ -144,6 +146,27 @@ int mfa_decode_attn(const void* q, const void* k_cache, const void* v_cache, con
                     const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale,
                     void* out, float* lse, void* ws, size_t ws_bytes, int B, int num_workgroups,
                     mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
+
+/* ------------------------------------------------------------------ attention, no allocation
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Computes exactly what mfa_decode_attn computes, with the same
+ * kernels and arguments, but its partial outputs and merge records go to a
+ * static device buffer the library owns, MFA_NOALLOC_SCRATCH_BYTES on every
+ * GPU it runs on (held until the process ends). Neither the call nor the
+ * kernels allocate or free anything. A call whose
+ * mfa_decode_attn_workspace_size(B, num_workgroups) exceeds the buffer
+ * returns MFA_ERR_WORKSPACE before any launch (with num_workgroups = 0, one
+ * per CU, up to about 380 sequences on 256 CUs). All calls on one GPU share
+ * its buffer, which keeps the last call's contents (nothing in it needs to
+ * start zeroed): calls that overlap on one GPU (other streams or threads)
+ * race, so the caller orders them. The buffer's device address is looked up
+ * on the first call on each device.
+ */
+#define MFA_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+int mfa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
+                            const int32_t* seq_len, float softmax_scale, float k_scale, float v_scale, void* out,
+                            float* lse, int B, int num_workgroups, mfa_dtype q_dt, mfa_dtype kv_dt, void* stream);
 
 /* ------------------------------------------------------------------ attention, several new tokens
  * Multi-token decode (speculative or multi-token-prediction verification;
