@@ -225,10 +225,13 @@ constexpr int kCpolNT = 2;
 // applied on the global side: slot (row r, chunk pc) receives global chunk
 // pc ^ swz(r). Each row is still read as one full run. Rows past the valid
 // end re-read the last valid row (their scores are masked to -inf).
-template <bool FP8, bool PAGED, int NT>
+// kIssuers waves share the DMAs of a tile (w = 0..kIssuers-1): the compute
+// waves themselves, or the producer waves.
+template <bool FP8, bool PAGED, int NT, int kIssuers = 4 * NT>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<FP8>::kRows, PAGED>& c, char* stage,
                                            int w, int lane) {
   using C = Cfg<FP8, NT>;
+  constexpr int kBlocks = C::kHalfBytes / 1024 / kIssuers;  // 1 KB blocks of K (and of V) per issuing wave
   long long lo, hi;
   c.tile(lo, hi);
   long long row0;  // cache row of the tile's first key
@@ -246,8 +249,8 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
   const int r_in = lane / C::kChunksPerRow;
   const int pc = lane % C::kChunksPerRow;
 #pragma unroll
-  for (int jj = 0; jj < C::kBlocksPerWave; ++jj) {
-    const int blk = w * C::kBlocksPerWave + jj;
+  for (int jj = 0; jj < kBlocks; ++jj) {
+    const int blk = w * kBlocks + jj;
     const int r = blk * C::kRowsPerBlock + r_in;
     const int rr = r < nvalid ? r : nvalid - 1;
     const int r32 = r & 31;
@@ -265,12 +268,13 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
 // prologue can wait for q and the first tile only, and the compiler never
 // sees q as a pending register load.
 // With NT tokens the NT q blocks of a sequence are contiguous ([B][NT][64][256]).
-template <int NT>
+template <int NT, int kIssuers = 4 * NT>
 __device__ __forceinline__ void issue_q(const AttnArgs& a, int b, char* qs, int w, int lane) {
   const char* src = (const char*)a.q + (long long)b * NT * (kHeads * kHeadDim * 2);
+  constexpr int kBlocks = 32 * NT / kIssuers;
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int blk = w * 8 + jj;  // 32 NT blocks of 1 KB, 8 per wave
+  for (int jj = 0; jj < kBlocks; ++jj) {
+    const int blk = w * kBlocks + jj;  // 32 NT blocks of 1 KB
     __builtin_amdgcn_global_load_lds((const void*)(src + blk * 1024 + lane * 16), (MFA_LDS void*)(qs + blk * 1024),
                                      16, 0, 0);
   }
@@ -693,6 +697,177 @@ __global__ __launch_bounds__(256 * NT, 1) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_tiles(int allowed) {
+  // tiles issued after the one needed that may stay in flight (N DMAs each)
+  if (allowed >= 3)
+    wait_vmcnt<3 * N>();
+  else if (allowed == 2)
+    wait_vmcnt<2 * N>();
+  else if (allowed == 1)
+    wait_vmcnt<N>();
+  else
+    wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
+// Output of one finished segment (a piece of sequence c.b, one new token):
+// the whole sequence is normalised and written directly; a split piece
+// writes its normalised bf16 partial and base-2 lse; the workgroup holding a
+// sequence's first piece records where its pieces are. lt and m are the
+// head's full row sum and reference max (base 2), lse_shift is subtracted
+// from the base-2 lse (the log2 of the units l is kept in).
+template <int kRows, bool PAGED>
+__device__ __forceinline__ void finish_segment(const AttnArgs& a, const Cursor<kRows, PAGED>& c, int wgi,
+                                               long long piece_lo, long long hi, int w, int lane, float lt, float m,
+                                               float lse_shift, const f32x4 (&acc)[16]) {
+  const int n = lane & 15, g = lane >> 4;
+  const float inv = a.v_mul / lt;
+  const float lse2 = m + fast_log2(lt) - lse_shift;
+  const int h = 16 * w + n;
+  const long long L = c.seq_end - c.seq_start;
+  if (piece_lo == 0 && threadIdx.x == 0) {
+    const int np = hi == L ? 0 : (int)((c.seq_start + L - 1) / c.per - wgi + 1);
+    *(i32x2*)(a.meta + 2 * c.b) = i32x2{wgi + c.b, np};
+  }
+  if (piece_lo == 0 && hi == L) {
+    bf16* orow = (bf16*)a.out + ((long long)c.b * kHeads + h) * kHeadDim + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      const bf16x4 o = {(bf16)(acc[db][0] * inv), (bf16)(acc[db][1] * inv), (bf16)(acc[db][2] * inv),
+                        (bf16)(acc[db][3] * inv)};
+      *(bf16x4*)(orow + 16 * db) = o;
+    }
+    if (a.lse != nullptr && g == 0) a.lse[(long long)c.b * kHeads + h] = lse2 * kLn2;
+  } else {
+    const long long slot = (long long)wgi + c.b;
+    bf16x8* prow = (bf16x8*)a.part_o + slot * (kHeads * kHeadDim / 8);
+#pragma unroll
+    for (int dp = 0; dp < 8; ++dp) {
+      const f32x4 v0 = acc[2 * dp] * inv, v1 = acc[2 * dp + 1] * inv;
+      prow[(w * 8 + dp) * 64 + lane] = bf16x8{(bf16)v0[0], (bf16)v0[1], (bf16)v0[2], (bf16)v0[3],
+                                              (bf16)v1[0], (bf16)v1[1], (bf16)v1[2], (bf16)v1[3]};
+    }
+    if (g == 0) a.part_lse[slot * kHeads + h] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One new token per sequence, with producer waves. Waves 0..3 compute (heads
+// 16w..16w+15, as in attn_mfma_kernel); kProducers more waves only move data:
+// they issue every DMA of the q blocks and the cache tiles into the LDS ring
+// and wait for their own, so a compute wave never stalls on a DMA issue (the
+// memory system takes requests only as fast as it drains them) and never
+// computes a DMA address. The per-tile barrier hands each landed tile from
+// the producers to the compute waves and each consumed stage back. Both
+// sides walk the same cursor, so they agree on every barrier, including the
+// two extra ones around a q reload when a piece reaches its next sequence.
+// Two producers keep three tiles in flight within the 6-bit wait counter.
+constexpr int kProducers = 2;
+
+// The producer side: the same cursor walk, the same barriers, only DMAs.
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::kRows, PAGED> prod, char* ring,
+                                            char* qs, int pw, int lane) {
+  using C = Cfg<FP8, 1>;
+  constexpr int kDpp = 2 * (C::kHalfBytes / 1024) / kProducers;  // DMAs per producer per tile
+  Cursor<C::kRows, PAGED> cons = prod;
+  int issued = 0;
+  issue_q<1, kProducers>(a, cons.b, qs, pw, lane);
+#pragma unroll
+  for (int st = 0; st < C::kStages - 1; ++st) {
+    if (prod.valid()) {
+      issue_tile<FP8, PAGED, 1, kProducers>(a, prod, ring + st * C::kTileBytes, pw, lane);
+      prod.advance(a.seq_len, a.seq_off);
+      ++issued;
+    }
+  }
+  // q and tile 0 have landed once at most the later prologue tiles are in flight
+  wait_tiles<kDpp>(issued - 1);
+  __builtin_amdgcn_s_barrier();
+  bool fresh = false;
+  for (int t = 0; cons.valid(); ++t) {
+    if (fresh) {
+      // every compute wave is done with the previous q once all meet here
+      __builtin_amdgcn_s_barrier();
+      issue_q<1, kProducers>(a, cons.b, qs, pw, lane);
+      wait_vmcnt<0>();  // (rare: drains the ring as well)
+      __builtin_amdgcn_s_barrier();
+      fresh = false;
+    }
+    wait_tiles<kDpp>(issued - t - 1);
+    __builtin_amdgcn_s_barrier();
+    if (prod.valid()) {
+      issue_tile<FP8, PAGED, 1, kProducers>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, pw,
+                                            lane);
+      prod.advance(a.seq_len, a.seq_off);
+      ++issued;
+    }
+    long long lo, hi;
+    cons.tile(lo, hi);
+    if (hi == cons.part_end() - cons.seq_start) fresh = true;
+    cons.advance(a.seq_len, a.seq_off);
+  }
+}
+
+template <bool FP8, bool PAGED>
+__global__ __launch_bounds__(64 * (4 + kProducers), 1) void attn_pc_kernel(AttnArgs a) {
+  using C = Cfg<FP8, 1>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::kLdsBytes];
+  char* const qs = ring + C::kStages * C::kTileBytes;
+  const int lane = threadIdx.x & 63;
+  const int wv = uniform((int)(threadIdx.x >> 6));
+  const int wgi = piece_index(a.G);
+
+  Cursor<C::kRows, PAGED> cons;
+  if (!init_cursor(a, wgi, lane, cons)) return;
+  if (wv >= 4) {
+    pc_producer<FP8, PAGED>(a, cons, ring, qs, wv - 4, lane);
+    return;
+  }
+  const int w = wv;  // heads 16w..16w+15
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  __builtin_amdgcn_s_barrier();  // q and tile 0 have landed
+  bf16x8 qf[8];
+  Q8 q8;
+  read_q<FP8>(qs, w, n, g, qf);
+  if constexpr (FP8) split_q8(qf, q8);
+  f32x4 acc[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const VReader<FP8> vr(n, g);
+  float m_run = -INFINITY, l_run = 0.f;
+  long long piece_lo = cons.gpos - cons.seq_start;
+  bool fresh = false;
+
+  for (int t = 0; cons.valid(); ++t) {
+    if (fresh) {
+      __builtin_amdgcn_s_barrier();  // done with the previous q
+      __builtin_amdgcn_s_barrier();  // the producers have loaded the next
+      read_q<FP8>(qs, w, n, g, qf);
+      if constexpr (FP8) split_q8(qf, q8);
+      m_run = -INFINITY;  // the first block rescales acc and l by exp2(-inf) = 0
+      piece_lo = cons.gpos - cons.seq_start;
+      fresh = false;
+    }
+    __builtin_amdgcn_s_barrier();  // tile t has landed
+    long long lo, hi;
+    cons.tile(lo, hi);
+    char* stage = ring + (t % C::kStages) * C::kTileBytes;
+    const int nvalid = cons.valid_rows(lo, hi);
+    if constexpr (FP8)
+      attend_tile_fp8<true>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, q8, a.score_mul, m_run, l_run, acc);
+    else
+      attend_tile_bf16(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
+    if (hi == cons.part_end() - cons.seq_start) {
+      finish_segment(a, cons, wgi, piece_lo, hi, w, lane, sum_over_rows(l_run), m_run, 0.f, acc);
+      fresh = true;
+    }
+    cons.advance(a.seq_len, a.seq_off);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 kernel (fp32 q and cache): plain VALU dot products, same work split and
 // partial format. Lane (n, g) of wave w owns head 16w+n and channels 64g..64g+63.
@@ -979,8 +1154,8 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
         e = p.table ? launch(attn_mfma_kernel<false, true, 2>, dim3(p.G), dim3(512), stream, a)
                     : launch(attn_mfma_kernel<false, false, 2>, dim3(p.G), dim3(512), stream, a);
       else
-        e = p.table ? launch(attn_mfma_kernel<false, true, 1>, dim3(p.G), block, stream, a)
-                    : launch(attn_mfma_kernel<false, false, 1>, dim3(p.G), block, stream, a);
+        e = p.table ? launch(attn_pc_kernel<false, true>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
+                    : launch(attn_pc_kernel<false, false>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
@@ -988,8 +1163,8 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
         e = p.table ? launch(attn_mfma_kernel<true, true, 2>, dim3(p.G), dim3(512), stream, a)
                     : launch(attn_mfma_kernel<true, false, 2>, dim3(p.G), dim3(512), stream, a);
       else
-        e = p.table ? launch(attn_mfma_kernel<true, true, 1>, dim3(p.G), block, stream, a)
-                    : launch(attn_mfma_kernel<true, false, 1>, dim3(p.G), block, stream, a);
+        e = p.table ? launch(attn_pc_kernel<true, true>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
+                    : launch(attn_pc_kernel<true, false>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
   }
