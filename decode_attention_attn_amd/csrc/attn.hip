@@ -763,21 +763,72 @@ __device__ __forceinline__ void finish_segment(const AttnArgs& a, const Cursor<k
 // sides walk the same cursor, so they agree on every barrier, including the
 // two extra ones around a q reload when a piece reaches its next sequence.
 // Two producers keep three tiles in flight within the 6-bit wait counter.
-constexpr int kProducers = 2;
+constexpr int kProducers = 2;  // producer waves per workgroup
+
+// DMA issue for the producer waves: the per-lane byte offsets of a full tile
+// (row and swizzled chunk, as issue_tile computes them) are computed once, so
+// a full tile costs one 64-bit uniform base and no per-lane address math;
+// tiles with rows past the end take issue_tile (rows clamped).
+template <bool FP8, bool PAGED, int kIssuers>
+struct TileIssuer {
+  using C = Cfg<FP8, 1>;
+  static constexpr int kBlocks = C::kHalfBytes / 1024 / kIssuers;
+  int koff[kBlocks], voff[kBlocks];
+  __device__ __forceinline__ TileIssuer(int w, int lane) {
+    const int r_in = lane / C::kChunksPerRow;
+    const int pc = lane % C::kChunksPerRow;
+#pragma unroll
+    for (int jj = 0; jj < kBlocks; ++jj) {
+      const int r = (w * kBlocks + jj) * C::kRowsPerBlock + r_in;
+      const int r32 = r & 31;
+      koff[jj] = r * C::kRowBytes + ((pc ^ swz_k(r32)) << 4);
+      voff[jj] = r * C::kRowBytes + ((pc ^ (FP8 ? swz_v8(r32) : swz_v16(r32))) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(const AttnArgs& a, const Cursor<C::kRows, PAGED>& c, char* stage, int w,
+                                        int lane) const {
+    long long lo, hi;
+    c.tile(lo, hi);
+    if (c.valid_rows(lo, hi) < C::kRows) {
+      issue_tile<FP8, PAGED, 1, kIssuers>(a, c, stage, w, lane);
+      return;
+    }
+    long long row0;
+    if constexpr (PAGED) {
+      const long long page = load_scalar(a.table, (long long)c.b * a.max_blocks + (lo >> a.page_shift));
+      row0 = (page << a.page_shift) + (lo & ((1LL << a.page_shift) - 1));
+    } else {
+      row0 = c.off + lo;
+    }
+    const char* kb = (const char*)a.k + uniform(row0) * C::kRowBytes;
+    const char* vb = (const char*)a.v + uniform(row0) * C::kRowBytes;
+#pragma unroll
+    for (int jj = 0; jj < kBlocks; ++jj) {
+      const int blk = w * kBlocks + jj;
+      __builtin_amdgcn_global_load_lds((const void*)(kb + koff[jj]), (MFA_LDS void*)(stage + blk * 1024), 16, 0,
+                                       kCpolNT);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + voff[jj]), (MFA_LDS void*)(stage + C::kHalfBytes + blk * 1024),
+                                       16, 0, kCpolNT);
+    }
+  }
+};
 
 // The producer side: the same cursor walk, the same barriers, only DMAs.
-template <bool FP8, bool PAGED>
+// b_guess: the sequence whose q the producers already requested before the
+// work split was known (exact for equal lengths); another is requested now.
+template <bool FP8, bool PAGED, int kNP>
 __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::kRows, PAGED> prod, char* ring,
-                                            char* qs, int pw, int lane) {
+                                            char* qs, int pw, int lane, int b_guess) {
   using C = Cfg<FP8, 1>;
-  constexpr int kDpp = 2 * (C::kHalfBytes / 1024) / kProducers;  // DMAs per producer per tile
+  constexpr int kDpp = 2 * (C::kHalfBytes / 1024) / kNP;  // DMAs per producer per tile
+  const TileIssuer<FP8, PAGED, kNP> tiles(pw, lane);
   Cursor<C::kRows, PAGED> cons = prod;
   int issued = 0;
-  issue_q<1, kProducers>(a, cons.b, qs, pw, lane);
+  if (cons.b != b_guess) issue_q<1, kNP>(a, cons.b, qs, pw, lane);  // lands after the guessed one
 #pragma unroll
   for (int st = 0; st < C::kStages - 1; ++st) {
     if (prod.valid()) {
-      issue_tile<FP8, PAGED, 1, kProducers>(a, prod, ring + st * C::kTileBytes, pw, lane);
+      tiles.issue(a, prod, ring + st * C::kTileBytes, pw, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
@@ -790,7 +841,7 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
     if (fresh) {
       // every compute wave is done with the previous q once all meet here
       __builtin_amdgcn_s_barrier();
-      issue_q<1, kProducers>(a, cons.b, qs, pw, lane);
+      issue_q<1, kNP>(a, cons.b, qs, pw, lane);
       wait_vmcnt<0>();  // (rare: drains the ring as well)
       __builtin_amdgcn_s_barrier();
       fresh = false;
@@ -798,8 +849,7 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
     wait_tiles<kDpp>(issued - t - 1);
     __builtin_amdgcn_s_barrier();
     if (prod.valid()) {
-      issue_tile<FP8, PAGED, 1, kProducers>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, pw,
-                                            lane);
+      tiles.issue(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, pw, lane);
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
@@ -810,19 +860,28 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
   }
 }
 
-template <bool FP8, bool PAGED>
-__global__ __launch_bounds__(64 * (4 + kProducers), 1) void attn_pc_kernel(AttnArgs a) {
+template <bool FP8, bool PAGED, int kNP>
+__global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) {
   using C = Cfg<FP8, 1>;
   __shared__ __attribute__((aligned(1024))) char ring[C::kLdsBytes];
   char* const qs = ring + C::kStages * C::kTileBytes;
   const int lane = threadIdx.x & 63;
   const int wv = uniform((int)(threadIdx.x >> 6));
   const int wgi = piece_index(a.G);
+  // The producers request q before the work split is known, for the
+  // sequence this piece starts in when all lengths are equal, so that q
+  // travels during the split's round trip (if the guess is wrong the right q
+  // is requested once the split is known; q is only read after that).
+  const int b_guess = uniform((int)(((long long)wgi * a.B) / a.G));
+  if (wv >= 4) issue_q<1, kNP>(a, b_guess, qs, wv - 4, lane);
 
   Cursor<C::kRows, PAGED> cons;
-  if (!init_cursor(a, wgi, lane, cons)) return;
+  if (!init_cursor(a, wgi, lane, cons)) {
+    if (wv >= 4) wait_vmcnt<0>();  // no piece: let the q request land before leaving
+    return;
+  }
   if (wv >= 4) {
-    pc_producer<FP8, PAGED>(a, cons, ring, qs, wv - 4, lane);
+    pc_producer<FP8, PAGED, kNP>(a, cons, ring, qs, wv - 4, lane, b_guess);
     return;
   }
   const int w = wv;  // heads 16w..16w+15
@@ -1154,8 +1213,8 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
         e = p.table ? launch(attn_mfma_kernel<false, true, 2>, dim3(p.G), dim3(512), stream, a)
                     : launch(attn_mfma_kernel<false, false, 2>, dim3(p.G), dim3(512), stream, a);
       else
-        e = p.table ? launch(attn_pc_kernel<false, true>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
-                    : launch(attn_pc_kernel<false, false>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
+        e = p.table ? launch(attn_pc_kernel<false, true, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
+                    : launch(attn_pc_kernel<false, false, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
@@ -1163,8 +1222,8 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
         e = p.table ? launch(attn_mfma_kernel<true, true, 2>, dim3(p.G), dim3(512), stream, a)
                     : launch(attn_mfma_kernel<true, false, 2>, dim3(p.G), dim3(512), stream, a);
       else
-        e = p.table ? launch(attn_pc_kernel<true, true>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
-                    : launch(attn_pc_kernel<true, false>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
+        e = p.table ? launch(attn_pc_kernel<true, true, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
+                    : launch(attn_pc_kernel<true, false, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
   }
