@@ -9,9 +9,10 @@ already resident in HBM:
     call, i.e. scores, online softmax, PV and the split merge;
   * ``*_paged`` attention workloads: the same keys in a paged cache (64-row
     pages in a shuffled order), one ``mfa_decode_attn_paged`` call;
-  * ``*_mtp2`` attention workloads: two new query tokens per sequence
-    (causal between them), one ``mfa_decode_attn_mt`` call; tokens/s counts
-    both; ``*_paged_mtp2``: both, one ``mfa_decode_attn_paged_mt`` call;
+  * ``*_mtpN`` attention workloads (N = 2, 3, 4): N new query tokens per
+    sequence (causal among them), one ``mfa_decode_attn_mt`` call; tokens/s
+    counts all of them; ``*_paged_mtpN``: both, one
+    ``mfa_decode_attn_paged_mt`` call;
   * ``layer_bf16_8k`` / ``layer_bf16_fp8kv_8k`` / ``layer_fp8_8k`` (block-fp8
     weights, e4m3 cache) / ``tiny_fp32``: the whole decode layer (q path, K/V
     append, attention, out-projection).
@@ -27,6 +28,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,7 +39,8 @@ METRIC = "MFA decode attn: KV-cache HBM GB/s (% of peak) + decode tokens/s at 4K
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 # Sources the attention kernels are built from: HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
-KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/attn.hip", "decode_attention_attn_amd/csrc/attn_core.h",
+KERNEL_SOURCES = ["decode_attention_attn_amd/csrc/attn.hip", "decode_attention_attn_amd/csrc/attn_mt.hip",
+                  "decode_attention_attn_amd/csrc/attn_core.h",
                   "decode_attention_attn_amd/csrc/mfa_common.h",
                   "decode_attention_attn_amd/csrc/mfa_internal.h", "decode_attention_attn_amd/build.py"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_traffic.json")
@@ -167,19 +170,41 @@ def _eager_time_ms(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps
 
 
+def _attn_base(name):
+    """(base workload, new tokens per sequence) of an attention workload name."""
+    m = re.search(r"_mtp(\d)$", name)
+    nt = int(m.group(1)) if m else 1
+    return re.sub(r"_mtp\d$", "", name).replace("_paged", ""), nt
+
+
+def _attn_kernels(name):
+    """What one timed attention call launches."""
+    _, nt = _attn_base(name)
+    entry = ("mfa_decode_attn_paged_mt" if "_paged" in name and nt > 1 else "mfa_decode_attn_paged"
+             if "_paged" in name else "mfa_decode_attn_mt" if nt > 1 else "mfa_decode_attn")
+    if "fp32" in name or name.startswith("tiny"):
+        body = "attn_f32_kernel + attn_combine_f32_kernel"
+    elif nt == 1:
+        body = "attn_pc_kernel + attn_combine_mfma_kernel"
+    elif nt == 2:
+        body = "attn_mt_kernel + attn_combine_mfma_kernel"
+    else:
+        body = "attn_mt_kernel (tokens 0-1) + attn_mt_kernel (the rest) + attn_combine_mfma_kernel"
+    return f"{entry} call = {body} (HIP events on the call's stream)"
+
+
 def bench_attn(name, steps, warmup, rotate, graph=True):
     import torch
 
     from decode_attention_attn_amd import inputs as gen
     from decode_attention_attn_amd import runner
 
-    base = name.replace("_paged", "").replace("_mtp2", "")
+    base, nt = _attn_base(name)
     w = gen.WORKLOADS[base]
     inp = gen.make_attn(w)
     if "_paged" in name:  # the same keys in 64-row pages, in a shuffled page order
         inp = gen.to_pages(inp, 64, seed=1)
-    nt = 2 if "_mtp2" in name else 1
-    if nt > 1:  # two new query tokens per sequence, causal between them
+    if nt > 1:  # nt new query tokens per sequence, causal among them
         inp = gen.with_tokens(inp, nt)
     dev = runner.upload_attn(inp)
     ks = [dev["k"]] + [dev["k"].clone() for _ in range(rotate - 1)]
@@ -306,9 +331,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn_bf16_4k",
                     choices=["attn_bf16_4k", "attn_fp8kv_4k", "attn_bf16_ragged", "attn_bf16_4k_paged",
-                             "attn_fp8kv_4k_paged", "attn_bf16_4k_mtp2", "attn_fp8kv_4k_mtp2", "attn_bf16_4k_paged_mtp2",
-                             "attn_fp8kv_4k_paged_mtp2", "layer_bf16_8k",
-                             "layer_bf16_fp8kv_8k", "layer_fp8_8k", "tiny_fp32"])
+                             "attn_fp8kv_4k_paged"]
+                    + [f"attn_{kv}_4k{pg}_mtp{n}" for kv in ("bf16", "fp8kv") for pg in ("", "_paged")
+                       for n in (2, 3, 4)]
+                    + ["layer_bf16_8k", "layer_bf16_fp8kv_8k", "layer_fp8_8k", "tiny_fp32"])
     ap.add_argument("--rotate", type=int, default=4, help="K/V buffer sets cycled through (attention workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -392,11 +418,7 @@ def main():
             # same call time as "achieved"; null when the kernel sources changed since the counters were taken
             "traffic": None if hbm_bytes is None else round(hbm_bytes / (ms * 1e-3) / 1e9, 2),
             "traffic_bytes_per_launch": hbm_bytes,
-            "kernel": ("mfa_decode_attn_paged_mt" if "_paged_mtp2" in res["workload"] else
-                       "mfa_decode_attn_paged" if "_paged" in res["workload"] else
-                       "mfa_decode_attn_mt" if "_mtp2" in res["workload"] else "mfa_decode_attn")
-            + " call = attn_mfma_kernel + attn_combine_mfma_kernel (HIP events on the call's stream)"
-            if w.kind == "attn" else "whole layer (HIP events)",
+            "kernel": _attn_kernels(res["workload"]) if w.kind == "attn" else "whole layer (HIP events)",
             "alg_bytes_per_launch": res["alg_bytes"],
         },
     }

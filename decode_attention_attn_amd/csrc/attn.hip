@@ -46,159 +46,10 @@
 #include "attn_core.h"
 
 namespace mfa {
-template <bool FP8, bool PAGED, int NT>
-__global__ __launch_bounds__(256 * NT, 1) void attn_mfma_kernel(AttnArgs a) {
-  using C = Cfg<FP8, NT>;
-  // the tile ring, then q (32 KB per token): 160 KB of LDS
-  __shared__ __attribute__((aligned(1024))) char ring[C::kLdsBytes];
-  char* const qs = ring + C::kStages * C::kTileBytes;
-  const int lane = threadIdx.x & 63;
-  const int wv = uniform((int)(threadIdx.x >> 6));
-  const int w = wv & 3;    // heads 16w..16w+15
-  const int tok = wv >> 2;  // new token (multi-token decode; 0 otherwise)
-  char* const qt = qs + tok * (kHeads * kHeadDim * 2);
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  const int wgi = piece_index(a.G);
-
-  Cursor<C::kRows, PAGED> prod;
-  if (!init_cursor(a, wgi, lane, prod)) return;
-  Cursor<C::kRows, PAGED> cons = prod;
-
-  // q of the first piece goes out ahead of the first tile DMAs.
-  issue_q<NT>(a, cons.b, qs, wv, lane);
-  int issued = 0;
-#pragma unroll
-  for (int s = 0; s < C::kStages - 1; ++s) {
-    if (prod.valid()) {
-      issue_tile<FP8, PAGED, NT>(a, prod, ring + s * C::kTileBytes, wv, lane);
-      prod.advance(a.seq_len, a.seq_off);
-      ++issued;
-    }
-  }
-  // q and tile 0 have landed once at most the later prologue tiles are in
-  // flight (DMAs complete in issue order); the loop's first step then refills
-  // right away.
-  if (issued == 3)
-    wait_vmcnt<2 * C::kDmaPerWave>();
-  else if (issued == 2)
-    wait_vmcnt<C::kDmaPerWave>();
-  else
-    wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-  bf16x8 qf[8];
-  read_q<FP8>(qt, w, n, g, qf);
-  Q8 q8;  // fp8 cache: q as hi/lo e4m3 pairs
-  if constexpr (FP8) split_q8(qf, q8);
-
-  f32x4 acc[16];
-#pragma unroll
-  for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const VReader<FP8> vr(n, g);
-  float m_run = -INFINITY, l_run = 0.f;
-  long long piece_lo = cons.gpos - cons.seq_start;
-  bool fresh = false;
-  bool drained = false;  // stores were issued since the last wait: drain fully
-
-  for (int t = 0; cons.valid(); ++t) {
-    if (fresh) {
-      // Later pieces of the workgroup: a full drain for their q (rare). Every
-      // wave finished reading the previous q right after it landed.
-      issue_q<NT>(a, cons.b, qs, wv, lane);
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      read_q<FP8>(qt, w, n, g, qf);
-      if constexpr (FP8) split_q8(qf, q8);
-      m_run = -INFINITY;  // the first block rescales acc by exp2(-inf) = 0
-      // (a token that sees no row of the new piece never rescales: its sum
-      // must start from zero for the empty-token test at the piece's end)
-      if constexpr (NT > 1) l_run = 0.f;
-      piece_lo = cons.gpos - cons.seq_start;
-      fresh = false;
-    }
-    if (!drained && issued - t - 1 >= C::kStages - 2)
-      wait_vmcnt<C::kSteadyVm>();
-    else
-      wait_vmcnt<0>();
-    drained = false;
-    __builtin_amdgcn_s_barrier();
-    if (prod.valid()) {
-      issue_tile<FP8, PAGED, NT>(a, prod, ring + ((t + C::kStages - 1) % C::kStages) * C::kTileBytes, wv, lane);
-      prod.advance(a.seq_len, a.seq_off);
-      ++issued;
-    }
-    char* stage = ring + (t % C::kStages) * C::kTileBytes;
-    long long lo, hi;
-    cons.tile(lo, hi);
-    int nvalid = cons.valid_rows(lo, hi);
-    if constexpr (NT > 1) {
-      // causal among the new tokens: token tok sees the rows before len - (NT - 1 - tok)
-      const long long lim = cons.len - (NT - 1 - tok);
-      nvalid = (int)((hi < lim ? hi : lim) - lo);
-    }
-    if (NT == 1 || nvalid > 0) {
-      if constexpr (FP8)
-        attend_tile_fp8<NT == 1>(stage, stage + C::kHalfBytes, nvalid, n, g, vr, q8, a.score_mul, m_run, l_run,
-                                 acc);
-      else
-        attend_tile_bf16(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
-    }
-
-    const long long pe = cons.part_end() - cons.seq_start;
-    if (hi == pe) {
-      // finalize this piece of sequence cons.b (for token tok)
-      const float lt = sum_over_rows(l_run);
-      float inv = a.v_mul / lt;
-      float lse2 = m_run + fast_log2(lt);
-      if constexpr (NT > 1) {
-        if (!(lt > 0.f)) {  // the token saw no row of this piece: weight 0 in the merge
-          inv = 0.f;
-          lse2 = -INFINITY;
-        }
-      }
-      const int h = 16 * w + n;
-      const long long bt = (long long)cons.b * NT + tok;  // output row of (sequence, token)
-      const long long L = cons.seq_end - cons.seq_start;
-      if (piece_lo == 0 && threadIdx.x == 0) {
-        // this workgroup holds the sequence's first piece: tell the combine
-        // where its pieces are (w0 = wgi; none when it is whole here)
-        const int np = hi == L ? 0 : (int)((cons.seq_start + L - 1) / cons.per - wgi + 1);
-        *(i32x2*)(a.meta + 2 * cons.b) = i32x2{wgi + cons.b, np};
-      }
-      if (piece_lo == 0 && hi == L) {
-        bf16* orow = (bf16*)a.out + (bt * kHeads + h) * kHeadDim + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-          const bf16x4 o = {(bf16)(acc[db][0] * inv), (bf16)(acc[db][1] * inv), (bf16)(acc[db][2] * inv),
-                            (bf16)(acc[db][3] * inv)};
-          *(bf16x4*)(orow + 16 * db) = o;
-        }
-        if (a.lse != nullptr && g == 0) a.lse[bt * kHeads + h] = lse2 * kLn2;
-      } else {
-        // partial outputs in bf16 (half the bytes of the round trip through
-        // memory; the merge weights stay fp32), in the register layout: one
-        // 1 KB contiguous store per wave and channel-block pair (the combine
-        // knows the map)
-        const long long slot = ((long long)wgi + cons.b) * NT + tok;
-        bf16x8* prow = (bf16x8*)a.part_o + slot * (kHeads * kHeadDim / 8);
-#pragma unroll
-        for (int dp = 0; dp < 8; ++dp) {
-          const f32x4 v0 = acc[2 * dp] * inv, v1 = acc[2 * dp + 1] * inv;
-          prow[(w * 8 + dp) * 64 + lane] = bf16x8{(bf16)v0[0], (bf16)v0[1], (bf16)v0[2], (bf16)v0[3],
-                                                  (bf16)v1[0], (bf16)v1[1], (bf16)v1[2], (bf16)v1[3]};
-        }
-        if (g == 0) a.part_lse[slot * kHeads + h] = lse2;
-      }
-      fresh = true;
-      drained = true;
-    }
-    cons.advance(a.seq_len, a.seq_off);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // One new token per sequence, with producer waves. Waves 0..3 compute (heads
-// 16w..16w+15, as in attn_mfma_kernel); kProducers more waves only move data:
+// 16w..16w+15); kProducers more waves only move data:
 // they issue every DMA of the q blocks and the cache tiles into the LDS ring
 // and wait for their own, so a compute wave never stalls on a DMA issue (the
 // memory system takes requests only as fast as it drains them) and never
@@ -215,7 +66,7 @@ constexpr int kProducers = 2;  // producer waves per workgroup
 // tiles with rows past the end take issue_tile (rows clamped).
 template <bool FP8, bool PAGED, int kIssuers>
 struct TileIssuer {
-  using C = Cfg<FP8, 1>;
+  using C = Cfg<FP8>;
   static constexpr int kBlocks = C::kHalfBytes / 1024 / kIssuers;
   int koff[kBlocks], voff[kBlocks];
   __device__ __forceinline__ TileIssuer(int w, int lane) {
@@ -234,7 +85,7 @@ struct TileIssuer {
     long long lo, hi;
     c.tile(lo, hi);
     if (c.valid_rows(lo, hi) < C::kRows) {
-      issue_tile<FP8, PAGED, 1, kIssuers>(a, c, stage, w, lane);
+      issue_tile<FP8, PAGED, kIssuers>(a, c, stage, w, lane);
       return;
     }
     long long row0;
@@ -263,12 +114,12 @@ struct TileIssuer {
 template <bool FP8, bool PAGED, int kNP>
 __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::kRows, PAGED> prod, char* ring,
                                             char* qs, int pw, int lane, int b_guess) {
-  using C = Cfg<FP8, 1>;
+  using C = Cfg<FP8>;
   constexpr int kDpp = 2 * (C::kHalfBytes / 1024) / kNP;  // DMAs per producer per tile
   const TileIssuer<FP8, PAGED, kNP> tiles(pw, lane);
   Cursor<C::kRows, PAGED> cons = prod;
   int issued = 0;
-  if (cons.b != b_guess) issue_q<1, kNP>(a, cons.b, qs, pw, lane);  // lands after the guessed one
+  if (cons.b != b_guess) issue_q<kNP>(a, cons.b, qs, pw, lane);  // lands after the guessed one
 #pragma unroll
   for (int st = 0; st < C::kStages - 1; ++st) {
     if (prod.valid()) {
@@ -285,7 +136,7 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
     if (fresh) {
       // every compute wave is done with the previous q once all meet here
       __builtin_amdgcn_s_barrier();
-      issue_q<1, kNP>(a, cons.b, qs, pw, lane);
+      issue_q<kNP>(a, cons.b, qs, pw, lane);
       wait_vmcnt<0>();  // (rare: drains the ring as well)
       __builtin_amdgcn_s_barrier();
       fresh = false;
@@ -306,7 +157,7 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
 
 template <bool FP8, bool PAGED, int kNP>
 __global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) {
-  using C = Cfg<FP8, 1>;
+  using C = Cfg<FP8>;
   __shared__ __attribute__((aligned(1024))) char ring[C::kLdsBytes];
   char* const qs = ring + C::kStages * C::kTileBytes;
   const int lane = threadIdx.x & 63;
@@ -317,7 +168,7 @@ __global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) 
   // travels during the split's round trip (if the guess is wrong the right q
   // is requested once the split is known; q is only read after that).
   const int b_guess = uniform((int)(((long long)wgi * a.B) / a.G));
-  if (wv >= 4) issue_q<1, kNP>(a, b_guess, qs, wv - 4, lane);
+  if (wv >= 4) issue_q<kNP>(a, b_guess, qs, wv - 4, lane);
 
   Cursor<C::kRows, PAGED> cons;
   if (!init_cursor(a, wgi, lane, cons)) {
@@ -554,8 +405,8 @@ __global__ __launch_bounds__(256) void attn_combine_f32_kernel(AttnArgs a) {
 __global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
   // workgroup (bt, y): channel block y of output row bt = (sequence b, token tok)
   const int bt = blockIdx.x;
-  const int nt = a.nt;  // 1, or 2 for multi-token decode
-  const int b = nt == 1 ? bt : bt >> 1;
+  const int nt = a.nt;  // new tokens per sequence (1 .. 4)
+  const int b = bt / nt;
   const int tok = bt - b * nt;
   const int c = blockIdx.y * 256 + threadIdx.x;
   const int lane = c & 63, dp = (c >> 6) & 7, w = c >> 9;
@@ -639,6 +490,7 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
   a.max_blocks = p.max_blocks;
   a.page_shift = p.page_shift;
   a.nt = p.nt;
+  a.t0 = 0;
   a.B = p.B;
   a.G = p.G;
   a.score_mul = p.softmax_scale * p.k_scale * kLog2e;
@@ -653,18 +505,16 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
       if (e == hipSuccess) e = launch(attn_combine_f32_kernel, comb_f32, block, stream, a);
       break;
     case AttnKind::BF16:
-      if (p.nt == 2)
-        e = p.table ? launch(attn_mfma_kernel<false, true, 2>, dim3(p.G), dim3(512), stream, a)
-                    : launch(attn_mfma_kernel<false, false, 2>, dim3(p.G), dim3(512), stream, a);
+      if (p.nt > 1)
+        e = launch_attn_mt(a, false, p.table != nullptr, stream);
       else
         e = p.table ? launch(attn_pc_kernel<false, true, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
                     : launch(attn_pc_kernel<false, false, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);
       if (e == hipSuccess) e = launch(attn_combine_mfma_kernel, comb_mfma, block, stream, a);
       break;
     case AttnKind::BF16_FP8KV:
-      if (p.nt == 2)
-        e = p.table ? launch(attn_mfma_kernel<true, true, 2>, dim3(p.G), dim3(512), stream, a)
-                    : launch(attn_mfma_kernel<true, false, 2>, dim3(p.G), dim3(512), stream, a);
+      if (p.nt > 1)
+        e = launch_attn_mt(a, true, p.table != nullptr, stream);
       else
         e = p.table ? launch(attn_pc_kernel<true, true, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a)
                     : launch(attn_pc_kernel<true, false, kProducers>, dim3(p.G), dim3(64 * (4 + kProducers)), stream, a);

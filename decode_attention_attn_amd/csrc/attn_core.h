@@ -26,7 +26,8 @@ struct AttnArgs {
   const int32_t* table;  // paged cache: [B][max_blocks] page of each page-sized block (null: contiguous)
   int max_blocks;
   int page_shift;        // page = 2^page_shift rows
-  int nt;                // new query tokens per sequence (1 or 2)
+  int nt;                // new query tokens per sequence (1 .. 4)
+  int t0;                // first token a multi-token launch handles (0: all of them)
   int B;
   int G;
   float score_mul;  // softmax_scale * k_scale * log2(e)
@@ -154,11 +155,10 @@ __device__ __forceinline__ bool init_cursor(const AttnArgs& a, int wgi, int lane
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel (bf16 q; bf16 or fp8 cache).
-// NT = new query tokens per sequence (1, or 2 for multi-token decode): wave w
-// serves token w / 4, heads 16 (w % 4)..+15, so NT tokens take 4 NT waves,
-// and their q (32 KB each) sit beside the ring.
-template <bool FP8, int NT = 1>
+// MFMA kernels (bf16 q; bf16 or fp8 cache): tile and ring geometry. Four
+// waves (heads 16w..16w+15 each) share a tile's DMAs unless producer waves
+// issue them; the one-token kernel keeps q (32 KB) beside the ring.
+template <bool FP8>
 struct Cfg {
   static constexpr int kRowBytes = FP8 ? 256 : 512;
   static constexpr int kRows = FP8 ? 64 : 32;                     // cache rows per tile
@@ -166,12 +166,11 @@ struct Cfg {
   static constexpr int kTileBytes = 2 * kHalfBytes;                // 32 KB
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kRowsPerBlock = 1024 / kRowBytes;           // rows per 1 KB DMA block
-  static constexpr int kWaves = 4 * NT;
-  static constexpr int kBlocksPerWave = kHalfBytes / 1024 / kWaves;  // DMA blocks per wave per half: 4 (2)
-  static constexpr int kDmaPerWave = 2 * kBlocksPerWave;             // DMA instructions per wave per tile: 8 (4)
-  static constexpr int kStages = NT == 1 ? 4 : 3;                    // LDS ring: 3 (2) tiles in flight
-  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;      // DMAs still in flight once a tile landed
-  static constexpr int kLdsBytes = kStages * kTileBytes + NT * kHeads * kHeadDim * 2;  // 160 KB
+  static constexpr int kWaves = 4;
+  static constexpr int kBlocksPerWave = kHalfBytes / 1024 / kWaves;  // DMA blocks per wave per half: 4
+  static constexpr int kDmaPerWave = 2 * kBlocksPerWave;             // DMA instructions per wave per tile: 8
+  static constexpr int kStages = 4;                                  // LDS ring: 3 tiles in flight
+  static constexpr int kLdsBytes = kStages * kTileBytes + kHeads * kHeadDim * 2;  // 160 KB
 };
 
 // XOR swizzles of 16-byte chunks within a row (row r = 0..31 of a 32-row block).
@@ -191,10 +190,10 @@ constexpr int kCpolNT = 2;
 // end re-read the last valid row (their scores are masked to -inf).
 // kIssuers waves share the DMAs of a tile (w = 0..kIssuers-1): the compute
 // waves themselves, or the producer waves.
-template <bool FP8, bool PAGED, int NT, int kIssuers = 4 * NT>
+template <bool FP8, bool PAGED, int kIssuers = 4>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<FP8>::kRows, PAGED>& c, char* stage,
                                            int w, int lane) {
-  using C = Cfg<FP8, NT>;
+  using C = Cfg<FP8>;
   constexpr int kBlocks = C::kHalfBytes / 1024 / kIssuers;  // 1 KB blocks of K (and of V) per issuing wave
   long long lo, hi;
   c.tile(lo, hi);
@@ -231,14 +230,13 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Cursor<Cfg<F
 // the cache tiles: it is then tracked by the same wait counts, so the
 // prologue can wait for q and the first tile only, and the compiler never
 // sees q as a pending register load.
-// With NT tokens the NT q blocks of a sequence are contiguous ([B][NT][64][256]).
-template <int NT, int kIssuers = 4 * NT>
+template <int kIssuers = 4>
 __device__ __forceinline__ void issue_q(const AttnArgs& a, int b, char* qs, int w, int lane) {
-  const char* src = (const char*)a.q + (long long)b * NT * (kHeads * kHeadDim * 2);
-  constexpr int kBlocks = 32 * NT / kIssuers;
+  const char* src = (const char*)a.q + (long long)b * (kHeads * kHeadDim * 2);
+  constexpr int kBlocks = 32 / kIssuers;
 #pragma unroll
   for (int jj = 0; jj < kBlocks; ++jj) {
-    const int blk = w * kBlocks + jj;  // 32 NT blocks of 1 KB
+    const int blk = w * kBlocks + jj;  // 32 blocks of 1 KB
     __builtin_amdgcn_global_load_lds((const void*)(src + blk * 1024 + lane * 16), (MFA_LDS void*)(qs + blk * 1024),
                                      16, 0, 0);
   }
@@ -388,12 +386,14 @@ __device__ __forceinline__ bf16x8 widen8(const i32x2& raw) {
   return v;
 }
 
-// Online-softmax update and value product of one 32-row block whose scores
-// (before score_mul) are s0 (rows 4g+i) and s1 (rows 16+4g+i) of head n; vf
-// holds the block's V^T operands. Rows at or past nvalid are masked (a block
-// with none left changes nothing once m_run is finite).
-__device__ __forceinline__ void softmax_pv(const f32x4& s0, const f32x4& s1, int nvalid, int g, float score_mul,
-                                           const bf16x8 (&vf)[16], float& m_run, float& l_run, f32x4 (&acc)[16]) {
+// Online-softmax update of one 32-row block whose scores (before score_mul)
+// are s0 (rows 4g+i) and s1 (rows 16+4g+i) of head n: the running max and
+// sum move, acc is rescaled when the max moves, and the block's exponentiated
+// scores come back as the B operand of its value product. Rows at or past
+// nvalid are masked (a block with none left changes nothing once m_run is
+// finite).
+__device__ __forceinline__ bf16x8 softmax_p(const f32x4& s0, const f32x4& s1, int nvalid, int g, float score_mul,
+                                            float& m_run, float& l_run, f32x4 (&acc)[16]) {
   float sc[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -420,7 +420,13 @@ __device__ __forceinline__ void softmax_pv(const f32x4& s0, const f32x4& s1, int
     p[i] = fast_exp2(sc[i] - m_run);
     l_run += p[i];
   }
-  const bf16x8 pf = {(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3], (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+  return bf16x8{(bf16)p[0], (bf16)p[1], (bf16)p[2], (bf16)p[3], (bf16)p[4], (bf16)p[5], (bf16)p[6], (bf16)p[7]};
+}
+
+// softmax_p, then the block's value product with its V^T operands vf.
+__device__ __forceinline__ void softmax_pv(const f32x4& s0, const f32x4& s1, int nvalid, int g, float score_mul,
+                                           const bf16x8 (&vf)[16], float& m_run, float& l_run, f32x4 (&acc)[16]) {
+  const bf16x8 pf = softmax_p(s0, s1, nvalid, g, score_mul, m_run, l_run, acc);
 #pragma unroll
   for (int db = 0; db < 16; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf, acc[db], 0, 0, 0);
 }
@@ -565,5 +571,9 @@ __device__ __forceinline__ void finish_segment(const AttnArgs& a, const Cursor<k
     if (g == 0) a.part_lse[slot * kHeads + h] = lse2;
   }
 }
+
+// Several new tokens per sequence, one cache fetch for all of them
+// (attn_mt.hip): a.nt = 2, 3 or 4, a.t0 = 0.
+hipError_t launch_attn_mt(const AttnArgs& a, bool fp8, bool paged, hipStream_t stream);
 
 }  // namespace mfa

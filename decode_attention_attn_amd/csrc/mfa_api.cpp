@@ -272,7 +272,7 @@ static int decode_attn_impl(const void* q, const void* k_cache, const void* v_ca
   const bool paged = block_table != nullptr;
   if (!q || !k_cache || !v_cache || (!paged && !seq_off) || !seq_len || !out || B < 1 || B > MFA_MAX_BATCH ||
       num_workgroups < 0 || num_workgroups > 65536 || !isfinite(softmax_scale) || !isfinite(k_scale) ||
-      !isfinite(v_scale) || n_tokens < 1 || n_tokens > 2)
+      !isfinite(v_scale) || n_tokens < 1 || n_tokens > MFA_MAX_TOKENS)
     return MFA_ERR_INVALID_ARG;
   int page_shift = 0;
   if (paged) {
@@ -352,7 +352,7 @@ int mfa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
 }
 
 size_t mfa_decode_attn_mt_workspace_size(int B, int n_tokens, int num_workgroups) {
-  if (n_tokens < 1 || n_tokens > 2) return 0;
+  if (n_tokens < 1 || n_tokens > MFA_MAX_TOKENS) return 0;
   const size_t one = mfa_decode_attn_workspace_size(B, num_workgroups);
   if (one == 0) return 0;
   int G = num_workgroups;

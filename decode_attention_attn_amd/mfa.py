@@ -38,6 +38,7 @@ MFA_OK, MFA_ERR_INVALID_ARG, MFA_ERR_UNSUPPORTED, MFA_ERR_ALIGNMENT, MFA_ERR_WOR
 MFA_HIDDEN, MFA_RANK, MFA_HEADS, MFA_HEAD_DIM = 7168, 2048, 64, 256
 MFA_QDIM = MFA_HEADS * MFA_HEAD_DIM
 MFA_MAX_BATCH = 65536
+MFA_MAX_TOKENS = 4
 
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 

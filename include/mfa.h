@@ -67,6 +67,8 @@ enum {
 
 /* Largest batch any call accepts. */
 #define MFA_MAX_BATCH 65536
+/* Most new query tokens per sequence the multi-token attention calls accept. */
+#define MFA_MAX_TOKENS 4
 
 int mfa_version(void);                       /* 10000 * major + 100 * minor + patch */
 const char* mfa_status_string(int status);   /* static string, never NULL */
@@ -177,10 +179,11 @@ int mfa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
  * [seq_off[b], seq_off[b] + seq_len[b] - (n_tokens - 1 - t)); otherwise as
  * mfa_decode_attn. q [B, n_tokens, 64, 256]; out [B, n_tokens, 64, 256];
  * lse [B, n_tokens, 64] or NULL. A token that sees no row gets out = 0 and
- * lse = -inf. n_tokens: 1 or 2 (else MFA_ERR_INVALID_ARG); 1 is exactly
- * mfa_decode_attn. Supported (q_dt, kv_dt): (BF16, BF16), (BF16, FP8_E4M3)
- * for n_tokens = 2. ws: at least mfa_decode_attn_mt_workspace_size(B,
- * n_tokens, num_workgroups) bytes (0 for invalid arguments).
+ * lse = -inf. n_tokens: 1 .. MFA_MAX_TOKENS (else MFA_ERR_INVALID_ARG); 1
+ * is exactly mfa_decode_attn. Supported (q_dt, kv_dt): (BF16, BF16),
+ * (BF16, FP8_E4M3) for n_tokens >= 2. Each key is fetched from memory once
+ * for tokens 0 and 1 and once more for tokens 2 .. n_tokens - 1. ws: at least mfa_decode_attn_mt_workspace_size(B, n_tokens,
+ * num_workgroups) bytes (0 for invalid arguments).
  */
 size_t mfa_decode_attn_mt_workspace_size(int B, int n_tokens, int num_workgroups);
 int mfa_decode_attn_mt(const void* q, const void* k_cache, const void* v_cache, const int64_t* seq_off,
@@ -214,7 +217,7 @@ int mfa_decode_attn_paged(const void* q, const void* k_pages, const void* v_page
  * mfa_decode_attn_mt, with sequence b's keys located through its block table
  * as in mfa_decode_attn_paged (token t sees the first seq_len[b] -
  * (n_tokens - 1 - t) keys of the sequence). Shapes, outputs, n_tokens
- * (1 or 2), supported dtypes and the workspace size
+ * (1 .. MFA_MAX_TOKENS), supported dtypes and the workspace size
  * (mfa_decode_attn_mt_workspace_size) are those of mfa_decode_attn_mt; the
  * page arguments and their preconditions are those of mfa_decode_attn_paged.
  * block_table NULL: MFA_ERR_INVALID_ARG.

@@ -29,6 +29,13 @@ def test_header_symbols_are_exported():
         assert mfa.raw_function(name) is not None
 
 
+def test_header_constants_match_the_binding():
+    src = open(os.path.join(ROOT, "include", "mfa.h")).read()
+    defs = dict(re.findall(r"#define\s+(MFA_[A-Z_]+)\s+(\d+)\s*$", src, re.M))
+    assert int(defs["MFA_MAX_BATCH"]) == mfa.MFA_MAX_BATCH
+    assert int(defs["MFA_MAX_TOKENS"]) == mfa.MFA_MAX_TOKENS
+
+
 def test_version_and_status_strings():
     assert mfa.mfa_version() == 10000
     for code in (0, -1, -2, -3, -4, -5):
@@ -107,16 +114,18 @@ def test_decode_attn_mt_rejects_bad_arguments():
         return f(a["q"], a["k"], a["v"], a["off"], a["len"], a["n"], 0.0625, 1.0, 1.0, a["out"], None, a["ws"],
                  a["nbytes"], a["B"], a["G"], a["qdt"], a["kvdt"], None)
 
-    for n in (0, 3, -1):
+    for n in (0, -1, mfa.MFA_MAX_TOKENS + 1, 1 << 30):
         assert call(n=n) == mfa.MFA_ERR_INVALID_ARG, n
     assert call(off=None) == mfa.MFA_ERR_INVALID_ARG
     assert call(qdt=mfa.MFA_F32, kvdt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
     assert call(q=MIS) == mfa.MFA_ERR_ALIGNMENT
-    need1 = mfa.mfa_decode_attn_mt_workspace_size(4, 1, 8)
-    need2 = mfa.mfa_decode_attn_mt_workspace_size(4, 2, 8)
-    assert need1 == mfa.mfa_decode_attn_workspace_size(4, 8) and need2 > need1
-    assert mfa.mfa_decode_attn_mt_workspace_size(4, 3, 8) == 0
-    assert call(nbytes=need2 - 1) == mfa.MFA_ERR_WORKSPACE
+    need = [mfa.mfa_decode_attn_mt_workspace_size(4, n, 8) for n in range(1, mfa.MFA_MAX_TOKENS + 1)]
+    assert need[0] == mfa.mfa_decode_attn_workspace_size(4, 8)
+    assert all(a < b for a, b in zip(need, need[1:])), need
+    for n in (0, -1, mfa.MFA_MAX_TOKENS + 1):
+        assert mfa.mfa_decode_attn_mt_workspace_size(4, n, 8) == 0, n
+    for n in range(2, mfa.MFA_MAX_TOKENS + 1):
+        assert call(n=n, nbytes=need[n - 1] - 1) == mfa.MFA_ERR_WORKSPACE, n
 
 
 def test_decode_attn_paged_mt_rejects_bad_arguments():
@@ -130,7 +139,7 @@ def test_decode_attn_paged_mt_rejects_bad_arguments():
                  a["out"], None, a["ws"], a["nbytes"], a["B"], a["G"], a["qdt"], a["kvdt"], None)
 
     assert call(table=None) == mfa.MFA_ERR_INVALID_ARG
-    for n in (0, 3):
+    for n in (0, mfa.MFA_MAX_TOKENS + 1):
         assert call(n=n) == mfa.MFA_ERR_INVALID_ARG, n
     assert call(maxb=0) == mfa.MFA_ERR_INVALID_ARG
     assert call(rows=100) == mfa.MFA_ERR_INVALID_ARG
@@ -138,7 +147,8 @@ def test_decode_attn_paged_mt_rejects_bad_arguments():
     assert call(qdt=mfa.MFA_FP8_E4M3) == mfa.MFA_ERR_UNSUPPORTED
     assert call(len=FAKE + 2) == mfa.MFA_ERR_ALIGNMENT
     assert call(ws=None) == mfa.MFA_ERR_WORKSPACE
-    assert call(nbytes=mfa.mfa_decode_attn_mt_workspace_size(4, 2, 8) - 1) == mfa.MFA_ERR_WORKSPACE
+    for n in range(2, mfa.MFA_MAX_TOKENS + 1):
+        assert call(n=n, nbytes=mfa.mfa_decode_attn_mt_workspace_size(4, n, 8) - 1) == mfa.MFA_ERR_WORKSPACE, n
 
 
 def test_projections_reject_bad_arguments():

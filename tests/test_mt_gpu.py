@@ -1,5 +1,6 @@
-"""GPU parity of mfa_decode_attn_mt (two new query tokens per sequence,
-causal between them) against the float64 oracle (needs an MI355X)."""
+"""GPU parity of mfa_decode_attn_mt and mfa_decode_attn_paged_mt (2 to 4 new
+query tokens per sequence, causal among them) against the float64 oracle
+(needs an MI355X)."""
 
 import numpy as np
 import pytest
@@ -14,8 +15,9 @@ from decode_attention_attn_amd import inputs as gen  # noqa: E402
 from oracle import mfa_oracle as om  # noqa: E402
 
 WL = {"bf16": gen.WORKLOADS["attn_bf16_4k"], "fp8_e4m3": gen.WORKLOADS["attn_fp8kv_4k"]}
-# length 1: the first token sees no row (output 0, lse -inf); 0: empty sequence
-LENGTHS = np.array([2, 1, 31, 32, 33, 100, 257, 0, 700, 65], dtype=np.int32)
+# lengths below n_tokens: the first tokens see no row (output 0, lse -inf);
+# 0: empty sequence
+LENGTHS = np.array([2, 1, 31, 32, 33, 100, 257, 0, 700, 65, 3, 4], dtype=np.int32)
 
 
 def _run(inp, G=0):
@@ -33,17 +35,18 @@ def _oracle(inp, ids=None):
                              v_scale=inp["v_scale"], batch_ids=ids)
 
 
+@pytest.mark.parametrize("nt", [2, 3, 4])
 @pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("G", [1, 3, 0])
-def test_two_tokens_small(kind, G):
-    print(f"[case] two tokens {kind} G={G} lengths={LENGTHS.tolist()}", flush=True)
+def test_tokens_small(nt, kind, G):
+    print(f"[case] {nt} tokens {kind} G={G} lengths={LENGTHS.tolist()}", flush=True)
     w = gen.scaled(WL[kind], batch=len(LENGTHS), ctx=0, seed=2)
-    inp = gen.with_tokens(gen.make_attn(w, lengths=LENGTHS), 2)
+    inp = gen.with_tokens(gen.make_attn(w, lengths=LENGTHS), nt)
     _, out, lse = _run(inp, G)
     o_ref, l_ref = _oracle(inp)
     t = TOL[kind]
-    check(f"two tokens out {kind} G={G}", out, o_ref, t["atol"], t["rel"])
-    check_lse(f"two tokens lse {kind} G={G}", lse, l_ref, t["lse"])
+    check(f"{nt} tokens out {kind} G={G}", out, o_ref, t["atol"], t["rel"])
+    check_lse(f"{nt} tokens lse {kind} G={G}", lse, l_ref, t["lse"])
 
 
 def _oracle_paged(pg, ids=None):
@@ -52,46 +55,49 @@ def _oracle_paged(pg, ids=None):
                                    k_scale=pg["k_scale"], v_scale=pg["v_scale"], batch_ids=ids)
 
 
+@pytest.mark.parametrize("nt", [2, 3, 4])
 @pytest.mark.parametrize("kind", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("page_rows,G", [(64, 1), (64, 0), (256, 3)])
-def test_two_tokens_paged_small(kind, page_rows, G):
-    # two tokens over shuffled pages whose unused rows hold NaN codes
-    print(f"[case] two tokens paged {kind} page_rows={page_rows} G={G} lengths={LENGTHS.tolist()}", flush=True)
+def test_tokens_paged_small(nt, kind, page_rows, G):
+    # several tokens over shuffled pages whose unused rows hold NaN codes
+    print(f"[case] {nt} tokens paged {kind} page_rows={page_rows} G={G} lengths={LENGTHS.tolist()}", flush=True)
     w = gen.scaled(WL[kind], batch=len(LENGTHS), ctx=0, seed=4)
-    pg = gen.to_pages(gen.with_tokens(gen.make_attn(w, lengths=LENGTHS), 2), page_rows, seed=6)
+    pg = gen.to_pages(gen.with_tokens(gen.make_attn(w, lengths=LENGTHS), nt), page_rows, seed=6)
     _, out, lse = _run(pg, G)
     o_ref, l_ref = _oracle_paged(pg)
     t = TOL[kind]
-    check(f"two tokens paged out {kind} R={page_rows} G={G}", out, o_ref, t["atol"], t["rel"])
-    check_lse(f"two tokens paged lse {kind} R={page_rows} G={G}", lse, l_ref, t["lse"])
+    check(f"{nt} tokens paged out {kind} R={page_rows} G={G}", out, o_ref, t["atol"], t["rel"])
+    check_lse(f"{nt} tokens paged lse {kind} R={page_rows} G={G}", lse, l_ref, t["lse"])
 
 
-@pytest.mark.parametrize("name,page_rows", [("attn_bf16_4k", 64), ("attn_fp8kv_4k", 128)])
-def test_two_tokens_paged_full_size(name, page_rows):
-    print(f"[case] two tokens paged {name} page_rows={page_rows} (full size, every sequence)", flush=True)
+@pytest.mark.parametrize("name,page_rows,nt", [("attn_bf16_4k", 64, 2), ("attn_fp8kv_4k", 128, 2),
+                                               ("attn_bf16_4k", 128, 3)])
+def test_tokens_paged_full_size(name, page_rows, nt):
+    print(f"[case] {nt} tokens paged {name} page_rows={page_rows} (full size, every sequence)", flush=True)
     w = gen.WORKLOADS[name]
-    pg = gen.to_pages(gen.with_tokens(gen.make_attn(w), 2), page_rows, seed=7)
+    pg = gen.to_pages(gen.with_tokens(gen.make_attn(w), nt), page_rows, seed=7)
     _, out, lse = _run(pg)
     o_ref, l_ref = _oracle_paged(pg)
     t = TOL[w.kv]
-    check(f"two tokens paged {name}", out, o_ref, t["atol"], t["rel"])
-    check_lse(f"two tokens paged {name} lse", lse, l_ref, t["lse"])
+    check(f"{nt} tokens paged {name}", out, o_ref, t["atol"], t["rel"])
+    check_lse(f"{nt} tokens paged {name} lse", lse, l_ref, t["lse"])
     for b in range(len(out)):
-        check(f"two tokens paged {name} out[{b}]", out[b], o_ref[b], t["atol"], t["rel"], quiet=True)
+        check(f"{nt} tokens paged {name} out[{b}]", out[b], o_ref[b], t["atol"], t["rel"], quiet=True)
 
 
-@pytest.mark.parametrize("name", ["attn_bf16_4k", "attn_fp8kv_4k"])
-def test_two_tokens_full_size(name):
-    print(f"[case] two tokens {name} (full size, every sequence)", flush=True)
+@pytest.mark.parametrize("name,nt", [("attn_bf16_4k", 2), ("attn_fp8kv_4k", 2), ("attn_bf16_4k", 4),
+                                     ("attn_fp8kv_4k", 4)])
+def test_tokens_full_size(name, nt):
+    print(f"[case] {nt} tokens {name} (full size, every sequence)", flush=True)
     w = gen.WORKLOADS[name]
-    inp = gen.with_tokens(gen.make_attn(w), 2)
+    inp = gen.with_tokens(gen.make_attn(w), nt)
     _, out, lse = _run(inp)
     o_ref, l_ref = _oracle(inp)
     t = TOL[w.kv]
-    check(f"two tokens {name}", out, o_ref, t["atol"], t["rel"])
-    check_lse(f"two tokens {name} lse", lse, l_ref, t["lse"])
+    check(f"{nt} tokens {name}", out, o_ref, t["atol"], t["rel"])
+    check_lse(f"{nt} tokens {name} lse", lse, l_ref, t["lse"])
     for b in range(len(out)):
-        check(f"two tokens {name} out[{b}]", out[b], o_ref[b], t["atol"], t["rel"], quiet=True)
+        check(f"{nt} tokens {name} out[{b}]", out[b], o_ref[b], t["atol"], t["rel"], quiet=True)
 
 
 def test_one_token_through_the_multi_token_entry_is_the_single_token_call():
