@@ -50,14 +50,14 @@ namespace mfa {
 // ---------------------------------------------------------------------------
 // One new token per sequence, with producer waves. Waves 0..3 compute (heads
 // 16w..16w+15); kProducers more waves only move data:
-// they issue every DMA of the q blocks and the cache tiles into the LDS ring
-// and wait for their own, so a compute wave never stalls on a DMA issue (the
+// they issue every DMA of the cache tiles (and of q, see kQLds) into the LDS
+// ring and wait for their own, so a compute wave never stalls on a DMA issue (the
 // memory system takes requests only as fast as it drains them) and never
 // computes a DMA address. The per-tile barrier hands each landed tile from
 // the producers to the compute waves and each consumed stage back. Both
-// sides walk the same cursor, so they agree on every barrier, including the
-// two extra ones around a q reload when a piece reaches its next sequence.
-// Two producers keep three tiles in flight within the 6-bit wait counter.
+// sides walk the same cursor, so they agree on every barrier.
+// Two producers keep three tiles in flight within the 6-bit wait counter
+// (measured: four producers, or a fifth ring stage, no faster).
 constexpr int kProducers = 2;  // producer waves per workgroup
 
 // DMA issue for the producer waves: the per-lane byte offsets of a full tile
@@ -108,18 +108,31 @@ struct TileIssuer {
   }
 };
 
+// Where the compute waves get q from. kQLds: the producers DMA it into an
+// LDS buffer beside the ring, as a tile (requested before the work split is
+// known, for the sequence the piece starts in when all lengths are equal),
+// and a piece's next sequence costs two extra barriers and a drain of the
+// ring. Otherwise the compute waves load it straight into registers (they
+// issue no other loads, so waiting for q never waits for a tile) and split it
+// for the fp8 product while the first tile is still in flight. Measured on
+// MI355X, 4K context: bf16 33.1 us with q in LDS against 33.6 us in
+// registers; fp8 cache 44.0 us against 42.8 us.
+template <bool FP8>
+constexpr bool kQLds = !FP8;
+
 // The producer side: the same cursor walk, the same barriers, only DMAs.
 // b_guess: the sequence whose q the producers already requested before the
-// work split was known (exact for equal lengths); another is requested now.
+// work split was known (kQLds only); another is requested now.
 template <bool FP8, bool PAGED, int kNP>
 __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::kRows, PAGED> prod, char* ring,
                                             char* qs, int pw, int lane, int b_guess) {
   using C = Cfg<FP8>;
   constexpr int kDpp = 2 * (C::kHalfBytes / 1024) / kNP;  // DMAs per producer per tile
+  static_assert((C::kStages - 1) * kDpp < 64, "tiles in flight exceed the wait counter");
   const TileIssuer<FP8, PAGED, kNP> tiles(pw, lane);
   Cursor<C::kRows, PAGED> cons = prod;
   int issued = 0;
-  if (cons.b != b_guess) issue_q<kNP>(a, cons.b, qs, pw, lane);  // lands after the guessed one
+  if (kQLds<FP8> && cons.b != b_guess) issue_q<kNP>(a, cons.b, qs, pw, lane);  // lands after the guessed one
 #pragma unroll
   for (int st = 0; st < C::kStages - 1; ++st) {
     if (prod.valid()) {
@@ -128,12 +141,14 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
       ++issued;
     }
   }
-  // q and tile 0 have landed once at most the later prologue tiles are in flight
-  wait_tiles<kDpp>(issued - 1);
-  __builtin_amdgcn_s_barrier();
+  if constexpr (kQLds<FP8>) {
+    // q and tile 0 have landed once at most the later prologue tiles are in flight
+    wait_tiles<kDpp>(issued - 1);
+    __builtin_amdgcn_s_barrier();
+  }
   bool fresh = false;
   for (int t = 0; cons.valid(); ++t) {
-    if (fresh) {
+    if (kQLds<FP8> && fresh) {
       // every compute wave is done with the previous q once all meet here
       __builtin_amdgcn_s_barrier();
       issue_q<kNP>(a, cons.b, qs, pw, lane);
@@ -141,6 +156,7 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
       __builtin_amdgcn_s_barrier();
       fresh = false;
     }
+    // tile t has landed once at most the later ones are in flight
     wait_tiles<kDpp>(issued - t - 1);
     __builtin_amdgcn_s_barrier();
     if (prod.valid()) {
@@ -158,34 +174,47 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
 template <bool FP8, bool PAGED, int kNP>
 __global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) {
   using C = Cfg<FP8>;
-  __shared__ __attribute__((aligned(1024))) char ring[C::kLdsBytes];
+  constexpr bool kQL = kQLds<FP8>;
+  __shared__ __attribute__((aligned(1024))) char ring[kQL ? C::kLdsBytes : C::kStages * C::kTileBytes];
   char* const qs = ring + C::kStages * C::kTileBytes;
   const int lane = threadIdx.x & 63;
   const int wv = uniform((int)(threadIdx.x >> 6));
   const int wgi = piece_index(a.G);
-  // The producers request q before the work split is known, for the
-  // sequence this piece starts in when all lengths are equal, so that q
-  // travels during the split's round trip (if the guess is wrong the right q
-  // is requested once the split is known; q is only read after that).
+  const int w = wv;  // compute waves: heads 16w..16w+15
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  // q is requested before the work split is known, for the sequence this
+  // piece starts in when all lengths are equal, so that it travels during the
+  // split's round trip (if the guess is wrong the right q is requested once
+  // the split is known; q is only read after that).
   const int b_guess = uniform((int)(((long long)wgi * a.B) / a.G));
-  if (wv >= 4) issue_q<kNP>(a, b_guess, qs, wv - 4, lane);
+  bf16x8 qf[8];
+  if constexpr (kQL) {
+    if (wv >= 4) issue_q<kNP>(a, b_guess, qs, wv - 4, lane);
+  } else {
+    if (wv < 4) load_q<FP8>(a, b_guess, w, n, g, qf);
+  }
 
   Cursor<C::kRows, PAGED> cons;
   if (!init_cursor(a, wgi, lane, cons)) {
-    if (wv >= 4) wait_vmcnt<0>();  // no piece: let the q request land before leaving
+    wait_vmcnt<0>();  // no piece: let the q request land before leaving
     return;
   }
   if (wv >= 4) {
     pc_producer<FP8, PAGED, kNP>(a, cons, ring, qs, wv - 4, lane, b_guess);
     return;
   }
-  const int w = wv;  // heads 16w..16w+15
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  __builtin_amdgcn_s_barrier();  // q and tile 0 have landed
-  bf16x8 qf[8];
   Q8 q8;
-  read_q<FP8>(qs, w, n, g, qf);
+  if constexpr (kQL) {
+    __builtin_amdgcn_s_barrier();  // q and tile 0 have landed
+    read_q<FP8>(qs, w, n, g, qf);
+  } else {
+    if (cons.b != b_guess) {
+      wait_vmcnt<0>();
+      load_q<FP8>(a, cons.b, w, n, g, qf);
+    }
+    wait_vmcnt<0>();
+  }
   if constexpr (FP8) split_q8(qf, q8);
   f32x4 acc[16];
 #pragma unroll
@@ -197,9 +226,15 @@ __global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) 
 
   for (int t = 0; cons.valid(); ++t) {
     if (fresh) {
-      __builtin_amdgcn_s_barrier();  // done with the previous q
-      __builtin_amdgcn_s_barrier();  // the producers have loaded the next
-      read_q<FP8>(qs, w, n, g, qf);
+      // the piece's next sequence: its q
+      if constexpr (kQL) {
+        __builtin_amdgcn_s_barrier();  // done with the previous q
+        __builtin_amdgcn_s_barrier();  // the producers have loaded the next
+        read_q<FP8>(qs, w, n, g, qf);
+      } else {
+        load_q<FP8>(a, cons.b, w, n, g, qf);
+        wait_vmcnt<0>();  // (also waits for the partial's stores just issued)
+      }
       if constexpr (FP8) split_q8(qf, q8);
       m_run = -INFINITY;  // the first block rescales acc and l by exp2(-inf) = 0
       piece_lo = cons.gpos - cons.seq_start;

@@ -255,6 +255,18 @@ __device__ __forceinline__ void read_q(const char* qs, int w, int n, int g, bf16
   }
 }
 
+// The same fragments straight from memory into registers: q row qrow
+// (sequence * nt + token) of [B * nt][64][256] bf16.
+template <bool FP8>
+__device__ __forceinline__ void load_q(const AttnArgs& a, long long qrow, int w, int n, int g, bf16x8 (&qf)[8]) {
+  const bf16* row = (const bf16*)a.q + (qrow * kHeads + 16 * w + n) * kHeadDim;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d0 = FP8 ? (128 * (j >> 2) + 32 * g + 8 * (j & 3)) : (32 * j + 8 * g);
+    qf[j] = *(const bf16x8*)(row + d0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp8 cache, score product: the cache's K bytes feed the gfx950 fp8 MFMA
 // (v_mfma_f32_16x16x128_f8f6f4, e4m3 operands, twice the bf16 rate) without
@@ -517,13 +529,15 @@ __device__ __forceinline__ void attend_tile_fp8(const char* ks, const char* vs, 
   softmax_pv(b0, b1, nvalid - 32, g, score_mul, vf, m_run, l_run, acc);
 }
 
-template <int N>
+template <int N, int kMax = 3>
 __device__ __forceinline__ void wait_tiles(int allowed) {
-  // tiles issued after the one needed that may stay in flight (N DMAs each)
-  if (allowed >= 3)
-    wait_vmcnt<3 * N>();
+  // tiles issued after the one needed that may stay in flight (N DMAs each;
+  // at most kMax of them exist)
+  static_assert(kMax >= 1 && kMax <= 3 && kMax * N < 64, "wait count range");
+  if (allowed >= kMax)
+    wait_vmcnt<kMax * N>();
   else if (allowed == 2)
-    wait_vmcnt<2 * N>();
+    wait_vmcnt<(kMax >= 2 ? 2 : 0) * N>();
   else if (allowed == 1)
     wait_vmcnt<N>();
   else

@@ -21,20 +21,12 @@
 
 namespace mfa {
 
-// q of head 16w + n for tokens tb .. tb + NT - 1 of sequence b, in the
-// layout read_q gives from LDS (see read_q): [B][nt][64][256] bf16 in memory.
+// q of head 16w + n for tokens tb .. tb + NT - 1 of sequence b.
 template <bool FP8, int NT>
 __device__ __forceinline__ void load_q_tokens(const AttnArgs& a, int b, int tb, int w, int n, int g,
                                               bf16x8 (&qf)[NT][8]) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const bf16* row = (const bf16*)a.q + (((long long)b * a.nt + tb + t) * kHeads + 16 * w + n) * kHeadDim;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d0 = FP8 ? (128 * (j >> 2) + 32 * g + 8 * (j & 3)) : (32 * j + 8 * g);
-      qf[t][j] = *(const bf16x8*)(row + d0);
-    }
-  }
+  for (int t = 0; t < NT; ++t) load_q<FP8>(a, (long long)b * a.nt + tb + t, w, n, g, qf[t]);
 }
 
 // One 32-row bf16 tile for NT tokens: each K fragment, read once, feeds the
