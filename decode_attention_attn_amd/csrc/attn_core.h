@@ -418,7 +418,10 @@ __device__ __forceinline__ bf16x8 softmax_p(const f32x4& s0, const f32x4& s1, in
   // more than 8 (base 2), so exponentials stay <= 256 (no bf16/fp32 range
   // issue) and the O rescale runs on a piece's first block and rarely after.
   const bool jump = mx > m_run + 8.f;
-  if (__ballot(jump)) {
+  if (__builtin_expect(__ballot(jump) != 0, 0)) {
+    // (an instruction with side effects keeps this a branch: without it the
+    // compiler executes the 64 accumulator multiplies on every block)
+    asm volatile("");
     const float m_new = jump ? mx : m_run;
     const float alpha = fast_exp2(m_run - m_new);  // 0 on a fresh piece (m_run = -inf)
     l_run *= alpha;
