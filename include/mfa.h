@@ -96,7 +96,9 @@ int mfa_qproj(const void* x, const void* w_dq, const float* gamma, float eps, co
  * seq_len_out: NULL, or a device int32 array of length B (4-byte aligned)
  * that receives seq_len[b] + 1, the length including the appended row, for
  * the attention call that follows; it may be seq_len itself (an in-place
- * increment, done after the row is written). Supported:
+ * increment, done after the row is written). Note: the call then mutates
+ * the lengths, which a plain append leaves to the caller; with seq_len_out
+ * NULL (or a separate array) seq_len is never written. Supported:
  * act_dt = cache_dt = MFA_F32, or act_dt = cache_dt = MFA_BF16.
  * Device-side precondition: the target rows exist and are distinct.
  * ws: at least mfa_kv_append_workspace_size(B, act_dt) bytes.
