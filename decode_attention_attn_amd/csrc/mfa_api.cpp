@@ -151,6 +151,61 @@ int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float
   return qproj_run(x, w_dq, s_dq, gamma, eps, w_uq, s_uq, q_out, ws, B, true, (hipStream_t)stream);
 }
 
+// ------------------------------------------------------------------ q path and K/V append in one
+size_t mfa_qproj_kv_append_workspace_size(int B) {
+  if (B < 1 || B > MFA_MAX_BATCH) return 0;
+  return mfa::qkv_layout(B).total;
+}
+
+int mfa_qproj_kv_append(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq,
+                        const void* w_k, const void* w_v, void* q_out, void* k_cache, void* v_cache,
+                        const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
+                        float v_scale, void* ws, size_t ws_bytes, int B, mfa_dtype cache_dt, void* stream) {
+  if (!x || !w_dq || !w_uq || !w_k || !w_v || !q_out || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 ||
+      B > MFA_MAX_BATCH || !(eps >= 0.f) || !isfinite(eps))
+    return MFA_ERR_INVALID_ARG;
+  if (cache_dt != MFA_BF16 && cache_dt != MFA_FP8_E4M3) return MFA_ERR_UNSUPPORTED;
+  const bool fp8 = cache_dt == MFA_FP8_E4M3;
+  float inv_k = 1.f, inv_v = 1.f;
+  if (fp8) {
+    // the stored byte is e4m3(x * (1 / scale)): the reciprocal must be finite and non-zero
+    inv_k = 1.f / k_scale;
+    inv_v = 1.f / v_scale;
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale) || !isfinite(inv_k) ||
+        !isfinite(inv_v) || !(inv_k > 0.f) || !(inv_v > 0.f))
+      return MFA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(w_k) || !aligned16(w_v) ||
+      !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws) || !aligned_n(seq_off, 8) ||
+      !aligned_n(seq_len, 4) || !aligned_n(seq_len_out, 4) || (gamma && !aligned_n(gamma, 4)))
+    return MFA_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < mfa_qproj_kv_append_workspace_size(B)) return MFA_ERR_WORKSPACE;
+  int st = MFA_OK;
+  const int cus = plan_cus(&st);
+  if (st != MFA_OK) return st;
+  const mfa::GemmPlan dn = mfa::plan_gemm(true, B, mfa::kPlanQkv, MFA_HIDDEN, MFA_RANK, cus);
+  const mfa::GemmPlan up = mfa::plan_gemm(true, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus);
+  const mfa::QprojLayout l = mfa::qkv_layout(B);
+  if (mfa::qproj_part_need(B, true, dn, up) > l.part_bytes) return MFA_ERR_WORKSPACE;  // a planning bug, never run
+  hipStream_t s = (hipStream_t)stream;
+  float* part = (float*)ws;
+  void* chat = (char*)ws + l.chat_offset;
+  // rows 0..2047 of the product from W_dq, 2048..2303 from W_k, 2304..2559 from W_v
+  hipError_t e = mfa::launch_gemm(true, dn, x, w_dq, w_k, part, mfa::GemmOut::Partial, s, nullptr, nullptr, w_v,
+                                  MFA_RANK + MFA_HEAD_DIM);
+  if (e != hipSuccess) return hip_status(e);
+  e = mfa::launch_qkv_epilogue(part, dn.splits, B, gamma, eps, chat, k_cache, v_cache, seq_off, seq_len, fp8, inv_k,
+                               inv_v, seq_len_out, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (up.splits > 1) {
+    // the first product's partials were consumed by the epilogue above
+    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s));
+  }
+  return hip_status(mfa::launch_gemm(true, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s));
+}
+
 // ------------------------------------------------------------------ K/V append
 size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt) {
   if (B < 1 || B > MFA_MAX_BATCH || !act_dtype_ok(act_dt)) return 0;

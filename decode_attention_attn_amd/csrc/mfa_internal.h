@@ -81,8 +81,10 @@ enum class GemmOut {
 };
 
 // S0 / S1 non-null: W0 / W1 are block-fp8 (e4m3 bytes, fp32 scales per 128 x 128 block, [rows/128][K/128])
+// W2 non-null (bf16 weights only): rows N0 <= n < N1 from W1, n >= N1 from W2.
 hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
-                       GemmOut mode, hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr);
+                       GemmOut mode, hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr,
+                       const void* W2 = nullptr, int N1 = 0);
 
 // c_hat[M, N] = rmsnorm(sum_s part[s]) * gamma, in the activation dtype.
 hipError_t launch_rmsnorm_reduce(bool bf16, const float* part, int S, int M, int N, const float* gamma,
@@ -92,6 +94,11 @@ hipError_t launch_sum_reduce(bool bf16, const float* part, int S, int M, int N, 
 // rows m: k = sum_s part[s][m][0:256], v = sum_s part[s][m][256:512] written at cache row off[m] + len[m].
 hipError_t launch_kv_scatter(bool bf16, const float* part, int S, int M, void* k_cache, void* v_cache,
                              const int64_t* seq_off, const int32_t* seq_len, int32_t* len_out, hipStream_t stream);
+// The [W_dq; W_k; W_v] product's partials [S][M][2560] (bf16 activations): c_hat[M, 2048] =
+// rmsnorm(columns 0..2047) * gamma, and the K/V rows (columns 2048..2559) written as the two scatters do.
+hipError_t launch_qkv_epilogue(const float* part, int S, int M, const float* gamma, float eps, void* chat,
+                               void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len,
+                               bool fp8_cache, float inv_k, float inv_v, int32_t* len_out, hipStream_t stream);
 // rows into e4m3 caches: byte = e4m3(clamp(x * inv, +-448)), round to nearest even
 hipError_t launch_kv_scatter_fp8(const float* part, int S, int M, void* k_cache, void* v_cache,
                                  const int64_t* seq_off, const int32_t* seq_len, float inv_k, float inv_v,

@@ -104,6 +104,20 @@ inline QprojLayout qproj_layout(int B, bool bf) {
   return l;
 }
 // Bytes of the q path's partial sums under one device's plans.
+// The q path with the K/V projections folded into its down-projection (one
+// GEMM over [W_dq; W_k; W_v], bf16 only): the same layout with 2560 columns
+// in the first product.
+constexpr int kPlanQkv = kPlanRank + 2 * kPlanHeadDim;
+inline QprojLayout qkv_layout(int B) {
+  QprojLayout l;
+  const size_t dn = gemm_partial_bound(B, kPlanQkv, kPlanHidden);
+  const size_t up = gemm_partial_bound(B, kPlanQDim, kPlanRank);
+  l.part_bytes = dn > up ? dn : up;
+  l.chat_offset = align256(l.part_bytes);
+  l.total = l.chat_offset + align256((size_t)B * kPlanRank * 2);
+  return l;
+}
+
 inline size_t qproj_part_need(int B, bool bf, const GemmPlan& dn, const GemmPlan& up) {
   if (!bf) return (size_t)B * kPlanRank * sizeof(float);
   size_t n = gemm_partial_bytes(dn);

@@ -44,6 +44,8 @@ struct GTile {
   static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;
 };
 
+// Weight rows n < N0 come from W0, N0 <= n < N1 from W1, n >= N1 from W2
+// (N1 = N: two matrices; bf16 weights only for a third one).
 struct GemmArgs {
   const bf16* X;
   const bf16* W0;  // (e4m3 bytes for block-fp8 weights)
@@ -52,6 +54,8 @@ struct GemmArgs {
   int M, N, K, N0, S;
   const float* S0;  // block-fp8: [rows / 128][K / 128] scales of W0 / W1
   const float* S1;
+  const bf16* W2;
+  int N1;
 };
 
 // 16-byte chunk swizzle for the 64-byte rows of a block-fp8 weight chunk:
@@ -95,7 +99,9 @@ __device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, in
       const int r = 8 * blk + r_in;
       const int c = pc ^ gswz(r);
       const int n = n0 + r;
-      const bf16* wrow = n < a.N0 ? a.W0 + (long long)n * a.K : a.W1 + (long long)(n - a.N0) * a.K;
+      const bf16* wrow = n < a.N0   ? a.W0 + (long long)n * a.K
+                         : n < a.N1 ? a.W1 + (long long)(n - a.N0) * a.K
+                                    : a.W2 + (long long)(n - a.N1) * a.K;
       __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0,
                                        kWCpol);
     } else {
@@ -403,14 +409,81 @@ __global__ __launch_bounds__(128) void kv_scatter_fp8_kernel(const float* part, 
   write_len_out(len_out, m, len);
 }
 
+// The down-projection and K/V products of one step from one GEMM over
+// [W_dq; W_k; W_v] (2048 + 256 + 256 columns): row m of the summed partials
+// gives c (columns 0..2047, RMS-normalized into c_hat as
+// rmsnorm_reduce_kernel does) and the new K and V rows (columns 2048..2559,
+// written as kv_scatter_kernel / kv_scatter_fp8_kernel do). One block of 512
+// threads per row; threads 0..127 also take 4 of the 512 K/V columns each.
+template <typename OutT, bool FP8KV>
+__global__ __launch_bounds__(512) void qkv_epilogue_kernel(const float* part, int S, int M, const float* gamma,
+                                                           float eps, OutT* chat, void* kc, void* vc,
+                                                           const int64_t* seq_off, const int32_t* seq_len,
+                                                           float inv_k, float inv_v, int32_t* len_out) {
+  constexpr int kN = 2560, kR = 2048;
+  const int m = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* prow = part + (long long)m * kN;
+  const long long stride = (long long)M * kN;
+  // K/V columns first, so their loads are in flight with the latent's
+  f32x4 kv = {0.f, 0.f, 0.f, 0.f};
+  if (t < 128) kv = sum_splits(prow + kR + 4 * t, stride, S);
+  const f32x4 c = sum_splits(prow + 4 * t, stride, S);
+  float ss = c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  __shared__ float red[8];
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3] + red[4] + red[5] + red[6] + red[7];
+  const float r = rsqrtf(tot / (float)kR + eps);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = c[e] * r;
+    if (gamma != nullptr) v *= gamma[4 * t + e];
+    chat[(long long)m * kR + 4 * t + e] = (OutT)v;
+  }
+  const int32_t len = seq_len[m];
+  if (t < 128) {
+    const int col = 4 * t;  // 0..508 of the [k | v] row
+    const long long row = seq_off[m] + (long long)len;
+    if constexpr (FP8KV) {
+      const float inv = col < 256 ? inv_k : inv_v;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q = kv[i] * inv;
+        x[i] = q > 448.f ? 448.f : (q < -448.f ? -448.f : q);
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+      *(int*)((unsigned char*)(col < 256 ? kc : vc) + row * 256 + (col & 255)) = w;
+    } else {
+      OutT* dst = (OutT*)(col < 256 ? kc : vc) + row * 256 + (col & 255);
+      dst[0] = (OutT)kv[0];
+      dst[1] = (OutT)kv[1];
+      dst[2] = (OutT)kv[2];
+      dst[3] = (OutT)kv[3];
+    }
+  }
+  write_len_out(len_out, m, len);
+}
+
 // ------------------------------------------------------------------ host side
 hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
-                       GemmOut mode, hipStream_t stream, const float* S0, const float* S1) {
+                       GemmOut mode, hipStream_t stream, const float* S0, const float* S1, const void* W2, int N1) {
+  if (W2 == nullptr) {
+    W2 = W1;
+    N1 = p.N;
+  } else if (!bf16_path || S0 != nullptr) {
+    return hipErrorInvalidValue;  // a third matrix only for bf16 weights
+  }
   if (!bf16_path) {
     return launch(gemm_f32_kernel, dim3((p.N + 3) / 4), dim3(256), stream, (const float*)X, (const float*)W0,
                        (const float*)W1, (float*)Y, p.M, p.N, p.K, p.N0);
   }
-  GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits, S0, S1};
+  GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits, S0, S1,
+             (const bf16*)W2, N1};
   const dim3 grid(p.N / p.tile_n, p.splits, p.mchunks);
   if (S0 != nullptr) {  // block-fp8 weights
     if (p.tile_n == 256)
@@ -455,6 +528,16 @@ hipError_t launch_kv_scatter(bool bf16_path, const float* part, int S, int M, vo
   else
     return launch(kv_scatter_kernel<float>, dim3(M), dim3(128), stream, part, S, M, (float*)k_cache,
                        (float*)v_cache, seq_off, seq_len, len_out);
+}
+
+hipError_t launch_qkv_epilogue(const float* part, int S, int M, const float* gamma, float eps, void* chat,
+                               void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len,
+                               bool fp8_cache, float inv_k, float inv_v, int32_t* len_out, hipStream_t stream) {
+  if (fp8_cache)
+    return launch(qkv_epilogue_kernel<bf16, true>, dim3(M), dim3(512), stream, part, S, M, gamma, eps, (bf16*)chat,
+                  k_cache, v_cache, seq_off, seq_len, inv_k, inv_v, len_out);
+  return launch(qkv_epilogue_kernel<bf16, false>, dim3(M), dim3(512), stream, part, S, M, gamma, eps, (bf16*)chat,
+                k_cache, v_cache, seq_off, seq_len, inv_k, inv_v, len_out);
 }
 
 hipError_t launch_kv_scatter_fp8(const float* part, int S, int M, void* k_cache, void* v_cache,

@@ -58,6 +58,10 @@ _lib.mfa_kv_append.restype = _I
 _lib.mfa_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _P]
 _lib.mfa_kv_append_fp8.restype = _I
 _lib.mfa_kv_append_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _Z, _I, _I, _P]
+_lib.mfa_qproj_kv_append_workspace_size.restype = _Z
+_lib.mfa_qproj_kv_append_workspace_size.argtypes = [_I]
+_lib.mfa_qproj_kv_append.restype = _I
+_lib.mfa_qproj_kv_append.argtypes = [_P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _F, _P, _Z, _I, _I, _P]
 _lib.mfa_decode_attn_workspace_size.restype = _Z
 _lib.mfa_decode_attn_workspace_size.argtypes = [_I, _I]
 _lib.mfa_decode_attn.restype = _I
@@ -90,6 +94,7 @@ EXPORTED = [
     "mfa_version", "mfa_status_string", "mfa_last_hip_error",
     "mfa_qproj_workspace_size", "mfa_qproj",
     "mfa_kv_append_workspace_size", "mfa_kv_append", "mfa_kv_append_fp8",
+    "mfa_qproj_kv_append_workspace_size", "mfa_qproj_kv_append",
     "mfa_decode_attn_workspace_size", "mfa_decode_attn", "mfa_decode_attn_noalloc", "mfa_decode_attn_paged",
     "mfa_decode_attn_paged_mt",
     "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
@@ -171,6 +176,18 @@ def mfa_kv_append_fp8(x, w_k, w_v, k_cache, v_cache, seq_off, seq_len, k_scale, 
     return _lib.mfa_kv_append_fp8(_ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off),
                                   _ptr(seq_len), _ptr(seq_len_out), float(k_scale), float(v_scale), _ptr(ws),
                                   _nbytes(ws), B, act_dt, _stream(stream))
+
+
+def mfa_qproj_kv_append_workspace_size(B: int) -> int:
+    return _lib.mfa_qproj_kv_append_workspace_size(B)
+
+
+def mfa_qproj_kv_append(x, w_dq, gamma, eps, w_uq, w_k, w_v, q_out, k_cache, v_cache, seq_off, seq_len, k_scale,
+                        v_scale, ws, B, cache_dt, stream=None, seq_len_out=None) -> int:
+    return _lib.mfa_qproj_kv_append(_ptr(x), _ptr(w_dq), _ptr(gamma), eps, _ptr(w_uq), _ptr(w_k), _ptr(w_v),
+                                    _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(seq_off), _ptr(seq_len),
+                                    _ptr(seq_len_out), float(k_scale), float(v_scale), _ptr(ws), _nbytes(ws), B,
+                                    cache_dt, _stream(stream))
 
 
 def mfa_decode_attn_workspace_size(B: int, num_workgroups: int = 0) -> int:

@@ -148,7 +148,7 @@ def upload_layer(inp: dict, device="cuda") -> dict:
 class LayerCall:
     """One decode step of the attention layer: q path, K/V append, attention, out-projection."""
 
-    def __init__(self, dev: dict, num_workgroups: int = 0, stream=None):
+    def __init__(self, dev: dict, num_workgroups: int = 0, stream=None, fused_q_kv: bool = True):
         self.dev = dev
         B = dev["B"]
         device = dev["x"].device
@@ -168,12 +168,36 @@ class LayerCall:
         self.ws_kv = _ws(mfa.mfa_kv_append_workspace_size(B, dt), device)
         self.ws_a = _ws(mfa.mfa_decode_attn_workspace_size(B, num_workgroups), device)
         self.ws_o = _ws(mfa.mfa_oproj_workspace_size(B, dt), device)
+        # bf16 activations and weights: the q path and the K/V append as one call
+        # (one product over [W_dq; W_k; W_v], mfa_qproj_kv_append)
+        self.fused = (fused_q_kv and dev["kind_w"] != FP8_BLOCK and dev["kind_act"] == BF16
+                      and dev["kind_kv"] in (BF16, FP8))
+        self.ws_qkv = _ws(mfa.mfa_qproj_kv_append_workspace_size(B), device) if self.fused else None
 
     def __call__(self):
         d, dt, s = self.dev, self.dt, self.stream
         B = d["B"]
         if d["kind_w"] == FP8_BLOCK:
             return self._call_w8()
+        if self.fused:
+            mfa.check(mfa.mfa_qproj_kv_append(d["x"], d["w_dq"], None, d["eps"], d["w_uq"], d["w_k"], d["w_v"], self.q,
+                                              d["k"], d["v"], d["off"], d["len"], d["k_scale"], d["v_scale"],
+                                              self.ws_qkv, B, _DT[d["kind_kv"]], s, seq_len_out=self.len_after),
+                      "mfa_qproj_kv_append")
+        else:
+            self._q_then_kv()
+        # the appended row is attended: the append wrote len + 1 into len_after
+        mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
+                                      d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
+                                      _DT[d["kind_kv"]], s),
+                  "mfa_decode_attn")
+        mfa.check(mfa.mfa_oproj(self.o, d["w_o"], self.y, self.ws_o, B, dt, s), "mfa_oproj")
+        return self
+
+    def _q_then_kv(self):
+        """The q path and the K/V append as two calls."""
+        d, dt, s = self.dev, self.dt, self.stream
+        B = d["B"]
         mfa.check(mfa.mfa_qproj(d["x"], d["w_dq"], None, d["eps"], d["w_uq"], self.q, self.ws_q, B, dt, s),
                   "mfa_qproj")
         if d["kind_kv"] == FP8:
@@ -183,13 +207,6 @@ class LayerCall:
         else:
             mfa.check(mfa.mfa_kv_append(d["x"], d["w_k"], d["w_v"], d["k"], d["v"], d["off"], d["len"], self.ws_kv,
                                         B, dt, _DT[d["kind_kv"]], s, seq_len_out=self.len_after), "mfa_kv_append")
-        # the appended row is attended: the append wrote len + 1 into len_after
-        mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
-                                      d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
-                                      _DT[d["kind_kv"]], s),
-                  "mfa_decode_attn")
-        mfa.check(mfa.mfa_oproj(self.o, d["w_o"], self.y, self.ws_o, B, dt, s), "mfa_oproj")
-        return self
 
     def _call_w8(self):
         # block-fp8 weights: the same four steps through the _w8 entry points

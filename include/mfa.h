@@ -108,6 +108,27 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
                   const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, void* ws, size_t ws_bytes,
                   int B, mfa_dtype act_dt, mfa_dtype cache_dt, void* stream);
 
+/* ------------------------------------------------------------------ q path and K/V append in one call
+ * mfa_qproj followed by mfa_kv_append (bf16 activations and weights) with
+ * the down-projection and the K/V projections, which all multiply x, done as
+ * one product over the stacked [W_dq; W_k; W_v] (2560 output columns) and
+ * one epilogue (RMSNorm of c, the K/V rows written at seq_off[b] +
+ * seq_len[b]); the q up-projection then follows as in mfa_qproj. The results
+ * are those of the two calls up to the order of fp32 additions (the K split
+ * of the stacked product is planned for its own shape). cache_dt = MFA_BF16
+ * (bf16 caches) or MFA_FP8_E4M3 (rows quantized as mfa_kv_append_fp8 does,
+ * with the host scales k_scale and v_scale; ignored for bf16). q_out, gamma,
+ * eps as for mfa_qproj; caches, seq_off, seq_len, seq_len_out and the
+ * device-side precondition as for mfa_kv_append. ws: at least
+ * mfa_qproj_kv_append_workspace_size(B) bytes (contents undefined on return).
+ * Other cache dtypes: MFA_ERR_UNSUPPORTED.
+ */
+size_t mfa_qproj_kv_append_workspace_size(int B);
+int mfa_qproj_kv_append(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq,
+                        const void* w_k, const void* w_v, void* q_out, void* k_cache, void* v_cache,
+                        const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
+                        float v_scale, void* ws, size_t ws_bytes, int B, mfa_dtype cache_dt, void* stream);
+
 /* ------------------------------------------------------------------ K/V append, e4m3 cache
  * As mfa_kv_append, but the rows are stored quantized into e4m3 caches (the
  * model runs in FP8, attention included: Step-3 summary, "Key claims"), the

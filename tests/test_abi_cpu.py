@@ -151,6 +151,34 @@ def test_decode_attn_paged_mt_rejects_bad_arguments():
         assert call(n=n, nbytes=mfa.mfa_decode_attn_mt_workspace_size(4, n, 8) - 1) == mfa.MFA_ERR_WORKSPACE, n
 
 
+def test_qproj_kv_append_rejects_bad_arguments():
+    f = mfa.raw_function("mfa_qproj_kv_append")
+
+    def call(**kw):
+        a = dict(x=FAKE, wdq=FAKE, gamma=None, eps=1e-6, wuq=FAKE, wk=FAKE, wv=FAKE, q=FAKE, kc=FAKE, vc=FAKE,
+                 off=FAKE, len=FAKE, lout=None, ks=1.0, vs=1.0, ws=FAKE, nbytes=1 << 40, B=4, cdt=mfa.MFA_BF16)
+        a.update(kw)
+        return f(a["x"], a["wdq"], a["gamma"], a["eps"], a["wuq"], a["wk"], a["wv"], a["q"], a["kc"], a["vc"],
+                 a["off"], a["len"], a["lout"], a["ks"], a["vs"], a["ws"], a["nbytes"], a["B"], a["cdt"], None)
+
+    need = mfa.mfa_qproj_kv_append_workspace_size(4)
+    assert need > 0 and mfa.mfa_qproj_kv_append_workspace_size(0) == 0
+    assert mfa.mfa_qproj_kv_append_workspace_size(mfa.MFA_MAX_BATCH + 1) == 0
+    for k in ("x", "wdq", "wuq", "wk", "wv", "q", "kc", "vc", "off", "len"):
+        assert call(**{k: None}) == mfa.MFA_ERR_INVALID_ARG, k
+    assert call(B=0) == mfa.MFA_ERR_INVALID_ARG
+    assert call(eps=-1.0) == mfa.MFA_ERR_INVALID_ARG
+    assert call(cdt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
+    assert call(cdt=mfa.MFA_FP8_E4M3, ks=0.0) == mfa.MFA_ERR_INVALID_ARG
+    assert call(cdt=mfa.MFA_FP8_E4M3, vs=float("inf")) == mfa.MFA_ERR_INVALID_ARG
+    # a bf16 cache ignores the scales: validation goes on to the workspace check
+    assert call(ks=0.0, nbytes=need - 1) == mfa.MFA_ERR_WORKSPACE
+    assert call(x=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert call(lout=FAKE + 2) == mfa.MFA_ERR_ALIGNMENT
+    assert call(ws=None) == mfa.MFA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == mfa.MFA_ERR_WORKSPACE
+
+
 def test_projections_reject_bad_arguments():
     qp = mfa.raw_function("mfa_qproj")
     assert qp(None, FAKE, None, 1e-6, FAKE, FAKE, FAKE, 1 << 30, 2, mfa.MFA_F32, None) == mfa.MFA_ERR_INVALID_ARG

@@ -23,13 +23,13 @@ from decode_attention_attn_amd import inputs as gen  # noqa: E402
 from oracle import mfa_oracle as om  # noqa: E402
 
 
-def _run_layer(inp, num_workgroups=0):
+def _run_layer(inp, num_workgroups=0, fused=True):
     from decode_attention_attn_amd import runner
 
     dev = runner.upload_layer(inp)
     k_before = dev["k"].clone()
     v_before = dev["v"].clone()
-    call = runner.LayerCall(dev, num_workgroups)
+    call = runner.LayerCall(dev, num_workgroups, fused_q_kv=fused)
     call()
     torch.cuda.synchronize()
     return runner, dev, call, k_before, v_before
@@ -52,9 +52,9 @@ def _stage_isolated_attn(runner, dev, call, inp, ids, chunk=16):
     return np.concatenate(outs), np.concatenate(lses)
 
 
-def _check_layer(inp, kind, ids=None, num_workgroups=0):
+def _check_layer(inp, kind, ids=None, num_workgroups=0, fused=True):
     """Every output of the sequences ``ids`` (all of them by default)."""
-    runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups)
+    runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups, fused)
     # the append hands attention the length including the new row
     assert torch.equal(call.len_after, dev["len"] + 1)
     t = TOL[kind]
@@ -177,8 +177,8 @@ def _check_codes(name, got, want, exact, scale):
     assert same.mean() >= 0.99, f"{name}: only {same.mean():.4f} of the codes agree"
 
 
-def _check_layer_fp8(inp, ids=None, num_workgroups=0):
-    runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups)
+def _check_layer_fp8(inp, ids=None, num_workgroups=0, fused=True):
+    runner, dev, call, k_before, v_before = _run_layer(inp, num_workgroups, fused)
     t, tb = TOL["fp8_e4m3"], TOL["bf16"]
     ids = list(range(len(inp["seq_len"]))) if ids is None else list(ids)
     ref = om.decode_layer(inp, batch_ids=ids)
@@ -204,6 +204,48 @@ def test_layer_fp8_cache_small(G):
     print(f"[case] layer bf16 with e4m3 cache B=5 ctx=300 G={G}", flush=True)
     w = gen.scaled(gen.WORKLOADS["layer_bf16_fp8kv_8k"], batch=5, ctx=300)
     _check_layer_fp8(gen.make_layer(w), num_workgroups=G)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+def test_layer_separate_q_and_kv_calls(cache):
+    # the layer step with mfa_qproj and mfa_kv_append(_fp8) as two calls (the
+    # default step makes them one mfa_qproj_kv_append call)
+    print(f"[case] layer B=5 ctx=300, {cache} cache, q path and K/V append as separate calls", flush=True)
+    name = "layer_bf16_8k" if cache == "bf16" else "layer_bf16_fp8kv_8k"
+    inp = gen.make_layer(gen.scaled(gen.WORKLOADS[name], batch=5, ctx=300))
+    if cache == "bf16":
+        _check_layer(inp, "bf16", fused=False)
+    else:
+        _check_layer_fp8(inp, fused=False)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("B", [3, 200])
+def test_fused_q_kv_call_matches_the_separate_calls(cache, B):
+    # the one-call q path + append against the two calls on the same inputs:
+    # q, the appended rows and the lengths agree to fp32 summation order
+    print(f"[case] mfa_qproj_kv_append vs mfa_qproj + append, {cache} cache, B={B}", flush=True)
+    name = "layer_bf16_8k" if cache == "bf16" else "layer_bf16_fp8kv_8k"
+    inp = gen.make_layer(gen.scaled(gen.WORKLOADS[name], batch=B, ctx=40))
+    _, dev_f, call_f, _, _ = _run_layer(inp, fused=True)
+    runner, dev_s, call_s, _, _ = _run_layer(inp, fused=False)
+    assert call_f.fused and not call_s.fused
+    assert torch.equal(call_f.len_after, call_s.len_after)
+    t = TOL["bf16"]
+    check("fused q", runner.to_f64(call_f.q), runner.to_f64(call_s.q), t["atol"], t["rel"])
+    rows = torch.as_tensor((inp["seq_off"] + inp["seq_len"]).astype(np.int64), device=dev_f["k"].device)
+    if cache == "bf16":
+        for nm in ("k", "v"):
+            check(f"fused {nm}_new", runner.to_f64(dev_f[nm][rows]), runner.to_f64(dev_s[nm][rows]), t["atol"],
+                  t["rel"])
+    else:
+        tab = om.e4m3fn_table()
+        for nm in ("k", "v"):
+            a, b = dev_f[nm][rows].cpu().numpy(), dev_s[nm][rows].cpu().numpy()
+            # codes may differ by one step where the fp32 value sits at a rounding midpoint
+            assert (a == b).mean() >= 0.99, f"{nm}: {(a != b).sum()} codes differ"
+            assert np.all(np.abs(tab[a] - tab[b]) <= 0.125 * np.abs(tab[b]) + 2.0 ** -9), nm
+    check("fused y", runner.to_f64(call_f.y), runner.to_f64(call_s.y), t["atol"], t["rel"])
 
 
 def test_layer_fp8_cache_full():
