@@ -21,11 +21,13 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmfa.so")
 SOURCES = ["attn.hip", "attn_mt.hip", "proj.hip", "probe.hip", "mfa_api.cpp"]
-# Per-source extra flags. The attention kernels keep their accumulators in
-# ordinary VGPRs as MFMA operands: with accumulators in AGPRs the compiler
-# copied all of them to VGPRs on every loop iteration for the rarely taken
-# online-softmax rescale (measured: 4-8% of the attention kernel's time).
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags. The attention and GEMM kernels keep their
+# accumulators in ordinary VGPRs as MFMA operands: with accumulators in AGPRs
+# the compiler copied all of them to VGPRs on every loop iteration, for the
+# rarely taken online-softmax rescale in attention (measured: 4-8% of the
+# attention kernel's time) and across the two fragment sets of the pipelined
+# GEMM loop.
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "proj.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

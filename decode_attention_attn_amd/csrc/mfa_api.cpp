@@ -94,12 +94,12 @@ size_t mfa_qproj_workspace_size(int B, mfa_dtype dt) {
 
 // The device's plans of the q path, checked against the reserved region
 // (a failed check would be a planning bug: it is reported, never run).
-static int qproj_plans(int B, bool bf, mfa::GemmPlan* dn, mfa::GemmPlan* up, mfa::QprojLayout* l) {
+static int qproj_plans(int B, bool bf, bool w8, mfa::GemmPlan* dn, mfa::GemmPlan* up, mfa::QprojLayout* l) {
   int st = MFA_OK;
   const int cus = plan_cus(&st);
   if (st != MFA_OK) return st;
-  *dn = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK, cus);
-  *up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus);
+  *dn = mfa::plan_gemm(bf, B, MFA_RANK, MFA_HIDDEN, MFA_RANK, cus, w8);
+  *up = mfa::plan_gemm(bf, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus, w8);
   *l = mfa::qproj_layout(B, bf);
   return mfa::qproj_part_need(B, bf, *dn, *up) <= l->part_bytes ? MFA_OK : MFA_ERR_WORKSPACE;
 }
@@ -108,7 +108,7 @@ static int qproj_run(const void* x, const void* w_dq, const float* s_dq, const f
                      const void* w_uq, const float* s_uq, void* q_out, void* ws, int B, bool bf, hipStream_t s) {
   mfa::GemmPlan plan, up;
   mfa::QprojLayout l;
-  const int st = qproj_plans(B, bf, &plan, &up, &l);
+  const int st = qproj_plans(B, bf, s_dq != nullptr, &plan, &up, &l);
   if (st != MFA_OK) return st;
   float* part = (float*)ws;
   void* chat = (char*)ws + l.chat_offset;
@@ -213,11 +213,11 @@ size_t mfa_kv_append_workspace_size(int B, mfa_dtype act_dt) {
 }
 
 // The device's plan of the [W_k; W_v] product, checked against the reserved region.
-static int kv_plan(int B, bool bf, mfa::GemmPlan* p) {
+static int kv_plan(int B, bool bf, bool w8, mfa::GemmPlan* p) {
   int st = MFA_OK;
   const int cus = plan_cus(&st);
   if (st != MFA_OK) return st;
-  *p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM, cus);
+  *p = mfa::plan_gemm(bf, B, 2 * MFA_HEAD_DIM, MFA_HIDDEN, MFA_HEAD_DIM, cus, w8);
   return mfa::kv_part_need(B, bf, *p) <= mfa::kv_ws_bytes(B, bf) ? MFA_OK : MFA_ERR_WORKSPACE;
 }
 
@@ -235,7 +235,7 @@ int mfa_kv_append(const void* x, const void* w_k, const void* w_v, void* k_cache
   if (!ws || ws_bytes < mfa_kv_append_workspace_size(B, act_dt)) return MFA_ERR_WORKSPACE;
   const bool bf = act_dt == MFA_BF16;
   mfa::GemmPlan plan;
-  const int st = kv_plan(B, bf, &plan);
+  const int st = kv_plan(B, bf, false, &plan);
   if (st != MFA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
@@ -264,7 +264,7 @@ int mfa_kv_append_fp8(const void* x, const void* w_k, const void* w_v, void* k_c
   if (!ws || ws_bytes < mfa_kv_append_workspace_size(B, act_dt)) return MFA_ERR_WORKSPACE;
   const bool bf = act_dt == MFA_BF16;
   mfa::GemmPlan plan;
-  const int st = kv_plan(B, bf, &plan);
+  const int st = kv_plan(B, bf, false, &plan);
   if (st != MFA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(bf, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s);
@@ -293,7 +293,7 @@ int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const voi
     return MFA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < mfa_kv_append_workspace_size(B, MFA_BF16)) return MFA_ERR_WORKSPACE;
   mfa::GemmPlan plan;
-  const int st = kv_plan(B, true, &plan);
+  const int st = kv_plan(B, true, true, &plan);
   if (st != MFA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = mfa::launch_gemm(true, plan, x, w_k, w_v, ws, mfa::GemmOut::Partial, s, s_k, s_v);
@@ -459,7 +459,7 @@ static int oproj_run(const void* attn, const void* w_o, const float* s_o, void* 
   int st = MFA_OK;
   const int cus = plan_cus(&st);
   if (st != MFA_OK) return st;
-  const mfa::GemmPlan plan = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN, cus);
+  const mfa::GemmPlan plan = mfa::plan_gemm(bf, B, MFA_HIDDEN, MFA_QDIM, MFA_HIDDEN, cus, s_o != nullptr);
   if (mfa::oproj_part_need(bf, plan) > ws_bytes) return MFA_ERR_WORKSPACE;  // within the documented size
   if (bf && plan.splits > 1) {
     hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s, s_o, s_o);

@@ -18,7 +18,9 @@ struct GemmPlan {
   int M, N, K, N0;
   int splits;   // S: the K dimension is cut into S parts, each adding fp32 partial sums
   int mchunks;  // ceil(M / 128) (bf16 path)
-  int tile_n;   // output columns per workgroup: 128 or 256 (bf16 path)
+  int tile_n;   // output columns per workgroup (bf16 path): 64 or 128 for bf16
+                // weights, 128 or 256 for block-fp8 weights
+  bool w8;      // made for block-fp8 weights
 };
 
 // Split-K factor of a tile width on `cus` compute units: the workgroups fill
@@ -35,16 +37,32 @@ inline int gemm_splits(int M, int N, int K, int tn, int cus) {
   return s;
 }
 
-// For each tile width, the split above; then the width with the smaller
-// estimated time: each CU streams (tile_n + 128) * K / S * 2 bytes of weights
-// and activations (~30 GB/s per CU), and the partial sums add 2 * S * M * N * 4
-// bytes across the chip (~5 TB/s). fp32 (VALU path): one plain pass, no split.
-inline GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) {
-  GemmPlan p{M, N, K, N0, 1, 1, kGemmTileN};
+// Activation bytes up to which a bf16-weight product takes 64-column tiles:
+// the 64-column tile reads two activation bytes per weight byte, which costs
+// nothing while the activations stay in L2 (q down-projection, K/V, q
+// up-projection at batch 128); the out-projection's 4 MB of activations take
+// 128-column tiles. Measured on MI355X at batch 128 (product + split-K sum):
+// q up 25.6 -> 18.4 us, [W_dq; W_k; W_v] 18.7 -> 15.2 us, out-projection
+// 61.5 -> 56.7 us against the block-fp8 kernel's tiling.
+constexpr long long kPipeSmallX = 2LL << 20;
+
+// bf16 weights: the tile width above and its split. Block-fp8 weights: for
+// each of the 128/256-column widths the split above, then the width with the
+// smaller estimated time: each CU streams (tile_n + 128) * K / S * 2 bytes of
+// weights and activations (~30 GB/s per CU), and the partial sums add
+// 2 * S * M * N * 4 bytes across the chip (~5 TB/s). fp32 (VALU path): one
+// plain pass, no split.
+inline GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus, bool w8 = false) {
+  GemmPlan p{M, N, K, N0, 1, 1, kGemmTileN, w8};
   if (!bf16_path) return p;
   if (cus < 1) cus = 1;
   if (cus > kPlanCus) cus = kPlanCus;
   p.mchunks = (M + kGemmTileM - 1) / kGemmTileM;
+  if (!w8) {
+    p.tile_n = (N % 128 != 0 || (long long)M * K * 2 <= kPipeSmallX) ? 64 : 128;
+    p.splits = gemm_splits(M, N, K, p.tile_n, cus);
+    return p;
+  }
   double best = 0.0;
   for (int tn = 128; tn <= 256; tn *= 2) {
     if (N % tn != 0) continue;
@@ -65,11 +83,12 @@ inline GemmPlan plan_gemm(bool bf16_path, int M, int N, int K, int N0, int cus) 
 
 inline size_t gemm_partial_bytes(const GemmPlan& p) { return (size_t)p.splits * p.M * p.N * sizeof(float); }
 
-// Partial-sum bytes that bound every bf16 plan of this product on 1..256
-// compute units: each width's split only grows with the CU count, so the
-// largest split of either width at 256 CUs bounds what any device picks.
+// Partial-sum bytes that bound every bf16 plan of this product, for either
+// weight format, on 1..256 compute units: the bf16-weight width does not
+// depend on the CU count and each width's split only grows with it, so the
+// largest split of any width at 256 CUs bounds what any device picks.
 inline size_t gemm_partial_bound(int M, int N, int K) {
-  size_t best = 0;
+  size_t best = (size_t)plan_gemm(true, M, N, K, N, kPlanCus, false).splits * M * N * sizeof(float);
   for (int tn = 128; tn <= 256; tn *= 2) {
     if (N % tn != 0) continue;
     const size_t b = (size_t)gemm_splits(M, N, K, tn, kPlanCus) * M * N * sizeof(float);

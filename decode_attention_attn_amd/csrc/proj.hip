@@ -256,6 +256,180 @@ __global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ bf16 weights
+// The product for bf16 weights. A workgroup of eight waves (two per SIMD)
+// owns TN weight rows x 128 batch rows and one K range; each 64-wide K chunk
+// of both operands goes HBM -> LDS by direct-to-LDS DMA into a ring, every
+// wave issuing its share, one barrier per chunk. Wave w owns 16 WN weight rows
+// x 16 WM batch rows. Measured on MI355X: LDS reads (about 128 B per clock
+// per CU) and MFMAs (16 clocks per 16x16x32 per SIMD) of one wave barely
+// overlap, and together they take about as long per chunk as the chunk's
+// weight bytes take to arrive, so the wave tile keeps LDS reads down
+// (each fragment feeds WM or WN MFMAs), two waves per SIMD fill each other's
+// gaps, and the second k-block's fragments are read while the first
+// k-block's MFMAs run. TN = 64 for products whose activations stay in L2, 128
+// (weights read nontemporal) for the out-projection.
+template <int TN, int WN, int WM>
+struct PTile {
+  static constexpr int kWaves = 8;
+  static constexpr int kWavesN = TN / (16 * WN);
+  static constexpr int kWavesM = 8 / WM;
+  static_assert(kWavesN * kWavesM == kWaves, "wave grid");
+  static constexpr int kWBytes = TN * 128;                 // weight rows x 64 bf16
+  static constexpr int kXBytes = kGM * 128;                // activation rows x 64 bf16
+  static constexpr int kStageBytes = kWBytes + kXBytes;
+  static constexpr int kFit = (150 * 1024) / kStageBytes;
+  static constexpr int kStages = kFit > 6 ? 6 : kFit;      // 64: 6 x 24 KB, 128: 4 x 32 KB
+  static constexpr int kDpw = kStageBytes / 1024 / kWaves;  // 1 KB DMAs per wave per chunk
+  static_assert((kStages - 1) * kDpw < 64, "DMAs in flight exceed the wait counter");
+};
+
+// lgkmcnt(0) only: this wave's LDS reads have completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+template <int TN, int WN, int WM>
+__device__ __forceinline__ void pipe_issue(const GemmArgs& a, int n0, int m0, int kc, char* stage, int w, int lane) {
+  using T = PTile<TN, WN, WM>;
+  const int r_in = lane >> 3;  // 8 rows of 128 B per 1 KB block
+  const int pc = lane & 7;
+  const int k0 = kc * kGK;
+  constexpr int kWBlocks = T::kWBytes / 1024;
+#pragma unroll
+  for (int jj = 0; jj < T::kDpw; ++jj) {
+    const int blk = T::kDpw * w + jj;  // weight blocks first, then activation blocks
+    if (blk < kWBlocks) {
+      const int r = 8 * blk + r_in;
+      const int n = n0 + r;
+      const bf16* wrow = n < a.N0   ? a.W0 + (long long)n * a.K
+                         : n < a.N1 ? a.W1 + (long long)(n - a.N0) * a.K
+                                    : a.W2 + (long long)(n - a.N1) * a.K;
+      // (the 128-column tile streams its weights nontemporal)
+      __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + (pc ^ gswz(r)) * 8),
+                                       (MFA_LDS void*)(stage + blk * 1024), 16, 0, TN == 128 ? 2 : 0);
+    } else {
+      const int r = 8 * (blk - kWBlocks) + r_in;
+      int m = m0 + r;
+      m = m < a.M ? m : a.M - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(a.X + (long long)m * a.K + k0 + (pc ^ gswz(r)) * 8),
+                                       (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
+    }
+  }
+}
+
+template <GemmOut MODE, int TN, int WN, int WM>
+__global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
+  using T = PTile<TN, WN, WM>;
+  __shared__ __attribute__((aligned(1024))) char ring[T::kStages * T::kStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform((int)(threadIdx.x >> 6));
+  const int wn = (wave % T::kWavesN) * 16 * WN;  // this wave's weight rows within the tile
+  const int wm = (wave / T::kWavesN) * 16 * WM;  // and batch rows
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = blockIdx.x * TN;
+  const int split = blockIdx.y;
+  const int m0 = blockIdx.z * kGM;
+  const int nch = a.K / kGK;
+  const int c_begin = (int)((long long)split * nch / a.S);
+  const int c_end = (int)((long long)(split + 1) * nch / a.S);
+  const int nloc = c_end - c_begin;
+
+  f32x4 acc[WN][WM];
+#pragma unroll
+  for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragments of k-block j (32 of the chunk's 64) of chunk t: lane (i16, g)
+  // holds elements 32j + 8g .. +7 of weight row 16nb + i16 / batch row 16mb + i16
+  auto frags = [&](int t, int j, bf16x8 (&wa)[WN], bf16x8 (&xb)[WM]) {
+    const char* st = ring + (t % T::kStages) * T::kStageBytes;
+    const char* ws = st + wn * 128;
+    const char* xs = st + T::kWBytes + wm * 128;
+    const int off = ((4 * j + g) ^ gswz(i16)) << 4;
+#pragma unroll
+    for (int nb = 0; nb < WN; ++nb) wa[nb] = lds_read_b128((const MFA_LDS bf16x8*)(ws + (16 * nb + i16) * 128 + off));
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb) xb[mb] = lds_read_b128((const MFA_LDS bf16x8*)(xs + (16 * mb + i16) * 128 + off));
+  };
+  auto mfmas = [&](const bf16x8 (&wa)[WN], const bf16x8 (&xb)[WM]) {
+#pragma unroll
+    for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nb], xb[mb], acc[nb][mb], 0, 0, 0);
+  };
+
+  // Every stage starts filled; afterwards chunk t + kStages goes into the
+  // stage of chunk t once all waves are past reading it.
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < T::kStages; ++s)
+    if (issued < nloc) {
+      pipe_issue<TN, WN, WM>(a, n0, m0, c_begin + issued, ring + s * T::kStageBytes, wave, lane);
+      ++issued;
+    }
+  bf16x8 wa0[WN], xb0[WM], wa1[WN], xb1[WM];
+  if (nloc > 0) {
+    if (issued == T::kStages)
+      wait_vmcnt<(T::kStages - 1) * T::kDpw>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    frags(0, 0, wa0, xb0);
+  }
+  // Explicit LDS waits at the loop head and tail keep the compiler's own
+  // wait analysis exact across the back edge (otherwise it waits for every
+  // read, including those meant to overlap the MFMAs).
+  wait_lds();
+  for (int t = 0; t + 1 < nloc; ++t) {
+    frags(t, 1, wa1, xb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(wa0, xb0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lds();  // done reading chunk t
+    // chunk t + 1 has landed once at most the chunks after it are in flight
+    if (issued - (t + 2) >= T::kStages - 2)
+      wait_vmcnt<(T::kStages - 2) * T::kDpw>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (issued < nloc) {
+      pipe_issue<TN, WN, WM>(a, n0, m0, c_begin + issued, ring + (issued % T::kStages) * T::kStageBytes, wave, lane);
+      ++issued;
+    }
+    frags(t + 1, 0, wa0, xb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(wa1, xb1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lds();
+  }
+  if (nloc > 0) {
+    frags(nloc - 1, 1, wa1, xb1);
+    mfmas(wa0, xb0);
+    mfmas(wa1, xb1);
+  }
+
+  // lane (i16, g), register i of acc[nb][mb] = Y[m0 + wm + 16mb + i16][n0 + wn + 16nb + 4g + i]
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb) {
+    const int m = m0 + wm + 16 * mb + i16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int nb = 0; nb < WN; ++nb) {
+      const int n = n0 + wn + 16 * nb + 4 * g;
+      if constexpr (MODE == GemmOut::Partial) {
+        float* dst = (float*)a.Y + ((long long)split * a.M + m) * a.N + n;
+        *(f32x4*)dst = acc[nb][mb];
+      } else {
+        bf16* dst = (bf16*)a.Y + (long long)m * a.N + n;
+        const bf16x4 o = {(bf16)acc[nb][mb][0], (bf16)acc[nb][mb][1], (bf16)acc[nb][mb][2], (bf16)acc[nb][mb][3]};
+        *(bf16x4*)dst = o;
+      }
+    }
+  }
+}
+
 // fp32 GEMV-style product: one wave per output column, rows of X in groups of 4.
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* X, const float* W0, const float* W1, float* Y,
                                                        int M, int N, int K, int N0) {
@@ -482,23 +656,29 @@ hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const v
     return launch(gemm_f32_kernel, dim3((p.N + 3) / 4), dim3(256), stream, (const float*)X, (const float*)W0,
                        (const float*)W1, (float*)Y, p.M, p.N, p.K, p.N0);
   }
+  // a plan is made for one weight format: block-fp8 plans use 128/256-column
+  // tiles, bf16 plans 64/128-column tiles of the pipelined kernel
+  if ((S0 != nullptr) != p.w8 || p.N % p.tile_n != 0) return hipErrorInvalidValue;
   GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits, S0, S1,
              (const bf16*)W2, N1};
   const dim3 grid(p.N / p.tile_n, p.splits, p.mchunks);
-  if (S0 != nullptr) {  // block-fp8 weights
+  const bool part = mode == GemmOut::Partial;
+  if (p.w8) {
     if (p.tile_n == 256)
-      return mode == GemmOut::Partial
-                 ? launch(gemm_bf16_kernel<GemmOut::Partial, 256, true>, grid, dim3(512), stream, a)
-                 : launch(gemm_bf16_kernel<GemmOut::Direct, 256, true>, grid, dim3(512), stream, a);
-    return mode == GemmOut::Partial ? launch(gemm_bf16_kernel<GemmOut::Partial, 128, true>, grid, dim3(256), stream, a)
-                                    : launch(gemm_bf16_kernel<GemmOut::Direct, 128, true>, grid, dim3(256), stream, a);
+      return part ? launch(gemm_bf16_kernel<GemmOut::Partial, 256, true>, grid, dim3(512), stream, a)
+                  : launch(gemm_bf16_kernel<GemmOut::Direct, 256, true>, grid, dim3(512), stream, a);
+    if (p.tile_n == 128)
+      return part ? launch(gemm_bf16_kernel<GemmOut::Partial, 128, true>, grid, dim3(256), stream, a)
+                  : launch(gemm_bf16_kernel<GemmOut::Direct, 128, true>, grid, dim3(256), stream, a);
+    return hipErrorInvalidValue;
   }
-  if (p.tile_n == 256) {
-    if (mode == GemmOut::Partial) return launch(gemm_bf16_kernel<GemmOut::Partial, 256>, grid, dim3(512), stream, a);
-    return launch(gemm_bf16_kernel<GemmOut::Direct, 256>, grid, dim3(512), stream, a);
-  }
-  if (mode == GemmOut::Partial) return launch(gemm_bf16_kernel<GemmOut::Partial, 128>, grid, dim3(256), stream, a);
-  return launch(gemm_bf16_kernel<GemmOut::Direct, 128>, grid, dim3(256), stream, a);
+  if (p.tile_n == 64)
+    return part ? launch(gemm_pipe_kernel<GemmOut::Partial, 64, 2, 2>, grid, dim3(512), stream, a)
+                : launch(gemm_pipe_kernel<GemmOut::Direct, 64, 2, 2>, grid, dim3(512), stream, a);
+  if (p.tile_n == 128)
+    return part ? launch(gemm_pipe_kernel<GemmOut::Partial, 128, 4, 2>, grid, dim3(512), stream, a)
+                : launch(gemm_pipe_kernel<GemmOut::Direct, 128, 4, 2>, grid, dim3(512), stream, a);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rmsnorm_reduce(bool bf16_path, const float* part, int S, int M, int N, const float* gamma, float eps,

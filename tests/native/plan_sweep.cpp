@@ -23,26 +23,36 @@ int main() {
         printf("q layout overlaps: B=%d bf=%d\n", B, bf);
         ++bad;
       }
-      for (int cus = 1; cus <= kPlanCus; ++cus) {
-        const GemmPlan dn = plan_gemm(bf, B, kPlanRank, kPlanHidden, kPlanRank, cus);
-        const GemmPlan up = plan_gemm(bf, B, kPlanQDim, kPlanRank, kPlanQDim, cus);
-        const GemmPlan kp = plan_gemm(bf, B, 2 * kPlanHeadDim, kPlanHidden, kPlanHeadDim, cus);
-        const GemmPlan opl = plan_gemm(bf, B, kPlanHidden, kPlanQDim, kPlanHidden, cus);
-        const size_t q_need = qproj_part_need(B, bf, dn, up);
-        if (q_need > ql.part_bytes) {
-          printf("q path: B=%d bf=%d cus=%d needs %zu > %zu\n", B, bf, cus, q_need, ql.part_bytes);
-          ++bad;
+      // bf16 weights and (bf16 activations only) block-fp8 weights
+      for (int w8 = 0; w8 <= bf; ++w8)
+        for (int cus = 1; cus <= kPlanCus; ++cus) {
+          const GemmPlan dn = plan_gemm(bf, B, kPlanRank, kPlanHidden, kPlanRank, cus, w8);
+          const GemmPlan up = plan_gemm(bf, B, kPlanQDim, kPlanRank, kPlanQDim, cus, w8);
+          const GemmPlan kp = plan_gemm(bf, B, 2 * kPlanHeadDim, kPlanHidden, kPlanHeadDim, cus, w8);
+          const GemmPlan opl = plan_gemm(bf, B, kPlanHidden, kPlanQDim, kPlanHidden, cus, w8);
+          const size_t q_need = qproj_part_need(B, bf, dn, up);
+          if (q_need > ql.part_bytes) {
+            printf("q path: B=%d bf=%d w8=%d cus=%d needs %zu > %zu\n", B, bf, w8, cus, q_need, ql.part_bytes);
+            ++bad;
+          }
+          if (kv_part_need(B, bf, kp) > kv) {
+            printf("kv: B=%d bf=%d w8=%d cus=%d needs %zu > %zu\n", B, bf, w8, cus, kv_part_need(B, bf, kp), kv);
+            ++bad;
+          }
+          if (oproj_part_need(bf, opl) > op) {
+            printf("oproj: B=%d bf=%d w8=%d cus=%d needs %zu > %zu\n", B, bf, w8, cus, oproj_part_need(bf, opl), op);
+            ++bad;
+          }
+          // a plan's tile divides its columns (the launcher rejects it otherwise)
+          const GemmPlan all[4] = {dn, up, kp, opl};
+          for (const GemmPlan& g : all)
+            if (bf && (g.N % g.tile_n != 0 || (w8 ? (g.tile_n != 128 && g.tile_n != 256)
+                                                   : (g.tile_n != 64 && g.tile_n != 128)))) {
+              printf("tile: B=%d w8=%d cus=%d N=%d tile %d\n", B, w8, cus, g.N, g.tile_n);
+              ++bad;
+            }
+          checked += 3;
         }
-        if (kv_part_need(B, bf, kp) > kv) {
-          printf("kv: B=%d bf=%d cus=%d needs %zu > %zu\n", B, bf, cus, kv_part_need(B, bf, kp), kv);
-          ++bad;
-        }
-        if (oproj_part_need(bf, opl) > op) {
-          printf("oproj: B=%d bf=%d cus=%d needs %zu > %zu\n", B, bf, cus, oproj_part_need(bf, opl), op);
-          ++bad;
-        }
-        checked += 3;
-      }
     }
     // the q path with the K/V projections folded in (bf16 only)
     const QprojLayout qk = qkv_layout(B);
