@@ -108,15 +108,18 @@ struct TileIssuer {
   }
 };
 
-// Where the compute waves get q from. kQLds: the producers DMA it into an
-// LDS buffer beside the ring, as a tile (requested before the work split is
-// known, for the sequence the piece starts in when all lengths are equal),
-// and a piece's next sequence costs two extra barriers and a drain of the
-// ring. Otherwise the compute waves load it straight into registers (they
-// issue no other loads, so waiting for q never waits for a tile) and split it
-// for the fp8 product while the first tile is still in flight. Measured on
-// MI355X, 4K context: bf16 33.1 us with q in LDS against 33.6 us in
-// registers; fp8 cache 44.0 us against 42.8 us.
+// Where the compute waves get q from. kQLds: the producers DMA the first q
+// of the piece into an LDS buffer beside the ring, as a tile (requested
+// before the work split is known, for the sequence the piece starts in when
+// all lengths are equal); once every compute wave has read a sequence's q into
+// registers (by the barrier of its second tile), the compute waves DMA the
+// next sequence's q into the same buffer, so a piece that runs into the next
+// sequence finds its q there without stopping the tile stream. Otherwise the
+// compute waves load q straight into registers (they issue no other loads, so
+// waiting for q never waits for a tile) and split it for the fp8 product
+// while the first tile is still in flight. Measured on MI355X, 4K context:
+// bf16 33.1 us with q in LDS against 33.6 us in registers; fp8 cache 44.0 us
+// against 42.8 us.
 template <bool FP8>
 constexpr bool kQLds = !FP8;
 
@@ -146,16 +149,7 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
     wait_tiles<kDpp>(issued - 1);
     __builtin_amdgcn_s_barrier();
   }
-  bool fresh = false;
   for (int t = 0; cons.valid(); ++t) {
-    if (kQLds<FP8> && fresh) {
-      // every compute wave is done with the previous q once all meet here
-      __builtin_amdgcn_s_barrier();
-      issue_q<kNP>(a, cons.b, qs, pw, lane);
-      wait_vmcnt<0>();  // (rare: drains the ring as well)
-      __builtin_amdgcn_s_barrier();
-      fresh = false;
-    }
     // tile t has landed once at most the later ones are in flight
     wait_tiles<kDpp>(issued - t - 1);
     __builtin_amdgcn_s_barrier();
@@ -164,9 +158,6 @@ __device__ __forceinline__ void pc_producer(const AttnArgs& a, Cursor<Cfg<FP8>::
       prod.advance(a.seq_len, a.seq_off);
       ++issued;
     }
-    long long lo, hi;
-    cons.tile(lo, hi);
-    if (hi == cons.part_end() - cons.seq_start) fresh = true;
     cons.advance(a.seq_len, a.seq_off);
   }
 }
@@ -223,24 +214,39 @@ __global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) 
   float m_run = -INFINITY, l_run = 0.f;
   long long piece_lo = cons.gpos - cons.seq_start;
   bool fresh = false;
+  int t_first = 0;  // the piece's first tile of the current sequence
+  int q_next = -1;  // kQL: the sequence whose q the compute waves put into the q buffer
 
   for (int t = 0; cons.valid(); ++t) {
-    if (fresh) {
+    if (!kQL && fresh) {
       // the piece's next sequence: its q
-      if constexpr (kQL) {
-        __builtin_amdgcn_s_barrier();  // done with the previous q
-        __builtin_amdgcn_s_barrier();  // the producers have loaded the next
-        read_q<FP8>(qs, w, n, g, qf);
-      } else {
-        load_q<FP8>(a, cons.b, w, n, g, qf);
-        wait_vmcnt<0>();  // (also waits for the partial's stores just issued)
-      }
+      load_q<FP8>(a, cons.b, w, n, g, qf);
+      wait_vmcnt<0>();  // (also waits for the partial's stores just issued)
       if constexpr (FP8) split_q8(qf, q8);
-      m_run = -INFINITY;  // the first block rescales acc and l by exp2(-inf) = 0
-      piece_lo = cons.gpos - cons.seq_start;
-      fresh = false;
     }
     __builtin_amdgcn_s_barrier();  // tile t has landed
+    if constexpr (kQL) {
+      if (fresh) {
+        // every compute wave waited for its part of the q DMA before the barrier
+        if (q_next == cons.b) {
+          read_q<FP8>(qs, w, n, g, qf);
+        } else {  // (a one-tile sequence before this one, or empty sequences between)
+          load_q<FP8>(a, cons.b, w, n, g, qf);
+          wait_vmcnt<0>();
+        }
+      } else if (t == t_first + 1 && cons.seq_end < cons.r1) {
+        // every compute wave has this sequence's q in registers (the previous
+        // tile's MFMAs consumed it): fetch the next sequence's q into the buffer
+        issue_q<4>(a, cons.b + 1, qs, w, lane);
+        q_next = cons.b + 1;
+      }
+    }
+    if (fresh) {
+      m_run = -INFINITY;  // the first block rescales acc and l by exp2(-inf) = 0
+      piece_lo = cons.gpos - cons.seq_start;
+      t_first = t;
+      fresh = false;
+    }
     long long lo, hi;
     cons.tile(lo, hi);
     char* stage = ring + (t % C::kStages) * C::kTileBytes;
@@ -250,6 +256,9 @@ __global__ __launch_bounds__(64 * (4 + kNP), 1) void attn_pc_kernel(AttnArgs a) 
     else
       attend_tile_bf16(stage, stage + C::kHalfBytes, nvalid, n, g, vr, qf, a.score_mul, m_run, l_run, acc);
     if (hi == cons.part_end() - cons.seq_start) {
+      // the next q's DMA (issued tiles ago) has landed: waited for here, before
+      // the partial's stores join the counter
+      if (kQL && q_next == cons.b + 1) wait_vmcnt<0>();
       finish_segment(a, cons, wgi, piece_lo, hi, w, lane, sum_over_rows(l_run), m_run, 0.f, acc);
       fresh = true;
     }
