@@ -447,12 +447,19 @@ __global__ __launch_bounds__(256) void attn_combine_f32_kernel(AttnArgs a) {
 // 32dp + 4(lane/16) + {0..3} and the same + 16. Grid (B, 8): thread c of the
 // sequence merges chunk c of every partial.
 __global__ __launch_bounds__(256) void attn_combine_mfma_kernel(AttnArgs a) {
-  // workgroup (bt, y): channel block y of output row bt = (sequence b, token tok)
-  const int bt = blockIdx.x;
+  // workgroup (bt, y): channel block y of output row bt = (sequence b, token tok).
+  // The attention kernel gives each XCD a contiguous run of pieces, so with
+  // equal lengths sequence b's pieces ran on XCD 8b / B; its merge is placed
+  // there too (workgroup i runs on XCD i % 8), where the partials may still
+  // be in L2. Placement only affects speed.
   const int nt = a.nt;  // new tokens per sequence (1 .. 4)
+  const int wgs = a.B * nt * 8;
+  const int i = blockIdx.x;
+  const int j = (a.B & 7) == 0 ? (i & 7) * (wgs >> 3) + (i >> 3) : i;
+  const int bt = j >> 3;
   const int b = bt / nt;
   const int tok = bt - b * nt;
-  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int c = (j & 7) * 256 + threadIdx.x;
   const int lane = c & 63, dp = (c >> 6) & 7, w = c >> 9;
   const int n = lane & 15, g = lane >> 4;
   const int h = 16 * w + n;
@@ -541,7 +548,7 @@ hipError_t launch_decode_attn(const AttnLaunch& p, hipStream_t stream) {
   a.v_mul = p.v_scale;
   const dim3 block(256);
   const dim3 comb_f32(p.B, 16);
-  const dim3 comb_mfma(p.B * p.nt, 8);
+  const dim3 comb_mfma(p.B * p.nt * 8);
   hipError_t e = hipSuccess;
   switch (p.kind) {
     case AttnKind::F32:

@@ -278,8 +278,10 @@ struct PTile {
   static constexpr int kWBytes = TN * 128;                 // weight rows x 64 bf16
   static constexpr int kXBytes = kGM * 128;                // activation rows x 64 bf16
   static constexpr int kStageBytes = kWBytes + kXBytes;
-  static constexpr int kFit = (150 * 1024) / kStageBytes;
-  static constexpr int kStages = kFit > 6 ? 6 : kFit;      // 64: 6 x 24 KB, 128: 4 x 32 KB
+  // three chunks in flight (measured on MI355X: five in flight for either width,
+  // or six stages of the 64-column tile, no faster; 64 columns 0.3-1.3 us slower)
+  static constexpr int kStages = 4;
+  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS");
   static constexpr int kDpw = kStageBytes / 1024 / kWaves;  // 1 KB DMAs per wave per chunk
   static_assert((kStages - 1) * kDpw < 64, "DMAs in flight exceed the wait counter");
 };
