@@ -533,6 +533,31 @@ __global__ __launch_bounds__(256) void sum_reduce_kernel(const float* part, int 
   dst[3] = (OutT)v[3];
 }
 
+// The same sum for a split product with bf16 weights, one workgroup per
+// tile_n columns x (1024 / tile_n) rows. The product's workgroup (x, split, m
+// chunk) ran on XCD x % 8 when the column-tile count is a multiple of 8
+// (workgroups are dealt round-robin to the 8 XCDs in launch order), so all
+// splits of column tile x sit in that XCD's L2: the sum of tile x is placed
+// on the same XCD. Placement only affects speed.
+template <typename OutT, int TN>
+__global__ __launch_bounds__(256) void sum_reduce_tiles_kernel(const float* part, int S, int M, int N, OutT* out) {
+  constexpr int kRows = 1024 / TN;
+  const int rblocks = (M + kRows - 1) / kRows;
+  const int tiles = N / TN;  // a multiple of 8
+  const int i = blockIdx.x;
+  const int x = i & 7, j = i >> 3;
+  const int tile = x + 8 * (j / rblocks);
+  const int m = (j % rblocks) * kRows + threadIdx.x / (TN / 4);
+  if (m >= M || tile >= tiles) return;
+  const int n = tile * TN + 4 * (threadIdx.x % (TN / 4));
+  const f32x4 v = sum_splits(part + (long long)m * N + n, (long long)M * N, S);
+  OutT* dst = out + (long long)m * N + n;
+  dst[0] = (OutT)v[0];
+  dst[1] = (OutT)v[1];
+  dst[2] = (OutT)v[2];
+  dst[3] = (OutT)v[3];
+}
+
 // The length including the appended row, for the attention call that
 // follows: written once every thread of the row's workgroup has read the old
 // length (len_out may be seq_len itself: an in-place increment).
@@ -693,7 +718,14 @@ hipError_t launch_rmsnorm_reduce(bool bf16_path, const float* part, int S, int M
                        (float*)out);
 }
 
-hipError_t launch_sum_reduce(bool bf16_path, const float* part, int S, int M, int N, void* out, hipStream_t stream) {
+hipError_t launch_sum_reduce(bool bf16_path, const float* part, int S, int M, int N, void* out, hipStream_t stream,
+                             int tile_n) {
+  if (bf16_path && (tile_n == 64 || tile_n == 128) && N % (8 * tile_n) == 0) {
+    const int rblocks = (M + 1024 / tile_n - 1) / (1024 / tile_n);
+    const dim3 grid((unsigned)((N / tile_n) * rblocks));
+    return tile_n == 64 ? launch(sum_reduce_tiles_kernel<bf16, 64>, grid, dim3(256), stream, part, S, M, N, (bf16*)out)
+                        : launch(sum_reduce_tiles_kernel<bf16, 128>, grid, dim3(256), stream, part, S, M, N, (bf16*)out);
+  }
   const long long total4 = (long long)M * N / 4;
   const dim3 grid((unsigned)((total4 + 255) / 256));
   if (bf16_path)
