@@ -58,9 +58,16 @@ struct GemmArgs {
   int N1;
 };
 
-// 16-byte chunk swizzle for the 64-byte rows of a block-fp8 weight chunk:
-// the 16 rows one MFMA fragment reads at a time land on distinct banks.
-__device__ __forceinline__ int gswz8(int r) { return (r >> 2) & 3; }
+// 16-byte chunk swizzle for the 64-byte rows of a block-fp8 weight chunk: a
+// fragment read takes one whole 16-byte chunk (16 k values) of 16 rows, and
+// the 8 lanes the LDS serves per clock (rows r..r+7 at one logical chunk) hit
+// 8 distinct 16-byte bank groups of the 128 bytes: rows two apart share a
+// 128-byte bank line, so the chunk position cycles with r >> 1.
+__device__ __forceinline__ int gswz8(int r) { return (r >> 1) & 3; }
+
+// 16-byte LDS read of raw bytes; the __restrict__ parameter keeps the compiler
+// from waiting for the in-flight LDS DMAs before it (as for lds_read_b128).
+__device__ __forceinline__ u32x4 lds_read_u128(const MFA_LDS u32x4* __restrict__ p) { return *p; }
 
 // 16-byte chunk swizzle for 128-byte rows: ds_read_b128 of 16 consecutive rows
 // at one logical chunk runs without bank conflicts on gfx950 (measured with
@@ -183,22 +190,30 @@ __global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
       const float sc = sc_next;
       sc_next = load_scalar(srow, (c_begin + (t + 1 < nloc ? t + 1 : t)) >> 1);
       const char* ws8 = ring + (t % kGStages) * kGStageBytes + wn * T::kWRow;
+      // The contraction order inside the chunk is free as long as both
+      // operands follow it: lane (i16, g) reads the whole 16-byte chunk g of
+      // its weight row (k = 16g .. 16g + 15) once, and MFMA j takes k = 16g +
+      // 8j .. +7 of it, the activation fragment the same k (logical 16-byte
+      // chunk 2g + j of the 128-byte activation row).
       f32x4 tmp[2][8];
+      u32x4 raw[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int r = 16 * nb + i16;
+        raw[nb] = lds_read_u128((const MFA_LDS u32x4*)(ws8 + r * 64 + ((g ^ gswz8(r)) << 4)));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int c = 4 * j + g;  // 8-element chunk of the 64: bytes 8c..8c+7 of the row
         bf16x8 wa[8], xb[2];
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const int r = 16 * nb + i16;
-          const u32x2 raw = *(const MFA_LDS u32x2*)(ws8 + r * 64 + ((((c >> 1) ^ gswz8(r))) << 4) + ((c & 1) << 3));
-          fp8x4_to_bf16(raw[0], wa[nb], 0);
-          fp8x4_to_bf16(raw[1], wa[nb], 4);
+          fp8x4_to_bf16(raw[nb][2 * j], wa[nb], 0);
+          fp8x4_to_bf16(raw[nb][2 * j + 1], wa[nb], 4);
         }
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
           const int r = 16 * (2 * w + mi) + i16;
-          xb[mi] = *(const MFA_LDS bf16x8*)(xs + r * 128 + ((c ^ gswz(r)) << 4));
+          xb[mi] = *(const MFA_LDS bf16x8*)(xs + r * 128 + (((2 * g + j) ^ gswz(r)) << 4));
         }
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
