@@ -6,12 +6,13 @@
 //
 // At decode time M = batch is small (2..128) and every weight byte is used M
 // times, so these products are bound by streaming the weights from HBM. The
-// bf16 kernel therefore tiles 128 weight rows x 128 batch rows per workgroup,
-// stages both operands through a 4-deep LDS ring filled by direct-to-LDS DMA
-// (weights read exactly once, as 128 B runs), and multiplies with
-// v_mfma_f32_16x16x32_bf16. The weight tile is the MFMA A operand, so each
-// lane ends up with four consecutive output columns of one batch row (one
-// 16-byte store). When the output tile count alone cannot fill the GPU, the
+// MFMA kernel therefore tiles 64..256 weight rows x 128 batch rows per
+// workgroup, stages both operands through a 4-deep LDS ring filled by
+// direct-to-LDS DMA (weights read exactly once), and multiplies with
+// v_mfma_f32_16x16x32_bf16 (block-fp8 weights are widened to bf16 in
+// registers and scaled per 128-wide K block). The weight tile is the MFMA A
+// operand, so each lane ends up with four consecutive output columns of one
+// batch row (one 16-byte store). When the output tile count alone cannot fill the GPU, the
 // K dimension is split and fp32 partial sums go to the workspace; a small
 // epilogue kernel adds them and applies what follows the product (RMSNorm of
 // the latent, the cache-row scatter of K/V, or the cast of y).
@@ -21,28 +22,8 @@
 
 namespace mfa {
 
-constexpr int kGN = kGemmTileN;  // output columns (weight rows) per workgroup (narrow tile)
 constexpr int kGM = kGemmTileM;  // batch rows per workgroup
 constexpr int kGK = kGemmChunkK; // K per stage
-
-// Tile shapes. Every wave owns 32 batch rows x 128 output columns. The wide
-// tile (8 waves, 256 columns) reads each activation chunk once per 256
-// weight rows instead of 128, which halves the activation share of the bytes
-// a workgroup streams; it is used for the wide products (the out-projection).
-// W8: block-fp8 weights (e4m3 bytes, 64-byte rows per chunk), widened to bf16
-// in registers; the ring then holds 4 stages of 24 KB or 32 KB.
-template <int NW, bool W8 = false>
-struct GTile {
-  static constexpr int kN = NW;                      // output columns per workgroup
-  static constexpr int kWaves = NW / 32;             // 4 or 8
-  static constexpr int kStages = (NW == 128 || W8) ? 4 : 3;
-  static constexpr int kWRow = W8 ? kGK : kGK * 2;   // bytes of one weight row per chunk
-  static constexpr int kWBytes = NW * kWRow;         // weight tile
-  static constexpr int kXBytes = kGM * kGK * 2;      // activation tile (16 KB)
-  static constexpr int kStageBytes = kWBytes + kXBytes;
-  static constexpr int kDmaPerWave = (kStageBytes / 1024) / kWaves;  // 8 or 6
-  static constexpr int kSteadyVm = (kStages - 2) * kDmaPerWave;
-};
 
 // Weight rows n < N0 come from W0, N0 <= n < N1 from W1, n >= N1 from W2
 // (N1 = N: two matrices; bf16 weights only for a third one).
@@ -75,204 +56,8 @@ __device__ __forceinline__ u32x4 lds_read_u128(const MFA_LDS u32x4* __restrict__
 // cycles per read).
 __device__ __forceinline__ int gswz(int r) { return r & 7; }
 
-// One K chunk of the weight tile (T::kN rows) and the activation tile (128
-// rows) into a ring stage: 1 KB blocks of 8 rows x 128 B, dealt evenly to
-// the waves (weight blocks first).
-template <int NW, bool W8>
-__device__ __forceinline__ void gemm_issue(const GemmArgs& a, int n0, int m0, int kc, char* stage, int w, int lane) {
-  using T = GTile<NW, W8>;
-  const int r_in = lane >> 3;  // 8 rows of 128 B per 1 KB block
-  const int pc = lane & 7;
-  const int k0 = kc * kGK;
-  constexpr int kWBlocks = T::kWBytes / 1024;
-  // Weight rows of the wide bf16 tile (the out-projection) stream with the
-  // nontemporal cache policy: 71 -> 66.5 us for it on MI355X; the same policy
-  // made the narrower and block-fp8 tiles slower (q path 44 -> 48 us), so they
-  // keep the default.
-  constexpr int kWCpol = (NW == 256 && !W8) ? 2 : 0;
-#pragma unroll
-  for (int jj = 0; jj < T::kDmaPerWave; ++jj) {
-    const int blk = T::kDmaPerWave * w + jj;
-    if (W8 && blk < kWBlocks) {
-      // 16 rows of 64 B per 1 KB block
-      const int r = 16 * blk + (lane >> 2);
-      const int c = (lane & 3) ^ gswz8(r);
-      const int n = n0 + r;
-      const unsigned char* wrow = n < a.N0 ? (const unsigned char*)a.W0 + (long long)n * a.K
-                                            : (const unsigned char*)a.W1 + (long long)(n - a.N0) * a.K;
-      __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 16), (MFA_LDS void*)(stage + blk * 1024), 16,
-                                       0, 0);
-    } else if (blk < kWBlocks) {
-      const int r = 8 * blk + r_in;
-      const int c = pc ^ gswz(r);
-      const int n = n0 + r;
-      const bf16* wrow = n < a.N0   ? a.W0 + (long long)n * a.K
-                         : n < a.N1 ? a.W1 + (long long)(n - a.N0) * a.K
-                                    : a.W2 + (long long)(n - a.N1) * a.K;
-      __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0,
-                                       kWCpol);
-    } else {
-      const int r = 8 * (blk - kWBlocks) + r_in;
-      const int c = pc ^ gswz(r);
-      int m = m0 + r;
-      m = m < a.M ? m : a.M - 1;
-      const bf16* xrow = a.X + (long long)m * a.K;
-      __builtin_amdgcn_global_load_lds((const void*)(xrow + k0 + c * 8), (MFA_LDS void*)(stage + blk * 1024), 16, 0,
-                                       0);
-    }
-  }
-}
-
-template <GemmOut MODE, int NW, bool W8 = false>
-__global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
-  using T = GTile<NW, W8>;
-  constexpr int kGStages = T::kStages;
-  constexpr int kGStageBytes = T::kStageBytes;
-  constexpr int kGSteadyVm = T::kSteadyVm;
-  __shared__ __attribute__((aligned(1024))) char ring[kGStages * kGStageBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int w = wave & 3;            // batch rows 32w..32w+31 of the tile
-  const int wn = (wave >> 2) * 128;  // this wave's 128 output columns within the tile
-  const int i16 = lane & 15;
-  const int g = lane >> 4;
-  const int n0 = blockIdx.x * T::kN;
-  const int split = blockIdx.y;
-  const int m0 = blockIdx.z * kGM;
-  const int nch = a.K / kGK;
-  const int c_begin = (int)((long long)split * nch / a.S);
-  const int c_end = (int)((long long)(split + 1) * nch / a.S);
-  const int nloc = c_end - c_begin;
-
-  f32x4 acc[2][8];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Block-fp8 weights: this wave's 128 weight rows form one row of scale
-  // blocks, so a 64-wide K chunk has one scale (blocks are 128 x 128). The
-  // row index is wave-uniform, so the scale reads are scalar loads, which do
-  // not touch the vector-memory counter the DMA ring waits on; each chunk's
-  // scale is read one chunk ahead.
-  const float* srow = nullptr;
-  float sc_next = 0.f;
-  if constexpr (W8) {
-    const int nrow = n0 + __builtin_amdgcn_readfirstlane(wn);
-    srow = nrow < a.N0 ? a.S0 + (long long)(nrow >> 7) * (a.K >> 7)
-                       : a.S1 + (long long)((nrow - a.N0) >> 7) * (a.K >> 7);
-    if (nloc > 0) sc_next = load_scalar(srow, c_begin >> 1);
-  }
-
-  int issued = 0;
-#pragma unroll
-  for (int s = 0; s < kGStages - 1; ++s)
-    if (issued < nloc) {
-      gemm_issue<NW, W8>(a, n0, m0, c_begin + issued, ring + s * kGStageBytes, wave, lane);
-      ++issued;
-    }
-
-  for (int t = 0; t < nloc; ++t) {
-    if (issued - t - 1 >= kGStages - 2)
-      wait_vmcnt<kGSteadyVm>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (issued < nloc) {
-      gemm_issue<NW, W8>(a, n0, m0, c_begin + issued, ring + ((t + kGStages - 1) % kGStages) * kGStageBytes, wave,
-                         lane);
-      ++issued;
-    }
-    const char* xs = ring + (t % kGStages) * kGStageBytes + T::kWBytes;
-    if constexpr (W8) {
-      // The chunk's product is formed from the exact bf16 widening of the
-      // bytes, then scaled into the accumulator in fp32.
-      const float sc = sc_next;
-      sc_next = load_scalar(srow, (c_begin + (t + 1 < nloc ? t + 1 : t)) >> 1);
-      const char* ws8 = ring + (t % kGStages) * kGStageBytes + wn * T::kWRow;
-      // The contraction order inside the chunk is free as long as both
-      // operands follow it: lane (i16, g) reads the whole 16-byte chunk g of
-      // its weight row (k = 16g .. 16g + 15) once, and MFMA j takes k = 16g +
-      // 8j .. +7 of it, the activation fragment the same k (logical 16-byte
-      // chunk 2g + j of the 128-byte activation row).
-      f32x4 tmp[2][8];
-      u32x4 raw[8];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int r = 16 * nb + i16;
-        raw[nb] = lds_read_u128((const MFA_LDS u32x4*)(ws8 + r * 64 + ((g ^ gswz8(r)) << 4)));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 wa[8], xb[2];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          fp8x4_to_bf16(raw[nb][2 * j], wa[nb], 0);
-          fp8x4_to_bf16(raw[nb][2 * j + 1], wa[nb], 4);
-        }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int r = 16 * (2 * w + mi) + i16;
-          xb[mi] = *(const MFA_LDS bf16x8*)(xs + r * 128 + (((2 * g + j) ^ gswz(r)) << 4));
-        }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb)
-            tmp[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                wa[nb], xb[mi], j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : tmp[mi][nb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[mi][nb] += tmp[mi][nb] * sc;
-      continue;
-    }
-    const char* ws = ring + (t % kGStages) * kGStageBytes + wn * 128;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = 4 * j + g;
-      bf16x8 wa[8], xb[2];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int r = 16 * nb + i16;
-        wa[nb] = *(const MFA_LDS bf16x8*)(ws + r * 128 + ((c ^ gswz(r)) << 4));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int r = 16 * (2 * w + mi) + i16;
-        xb[mi] = *(const MFA_LDS bf16x8*)(xs + r * 128 + ((c ^ gswz(r)) << 4));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-          acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nb], xb[mi], acc[mi][nb], 0, 0, 0);
-    }
-  }
-
-  // lane (i16, g), register i of acc[mi][nb] = Y[m0 + 16(2w+mi) + i16][n0 + 16nb + 4g + i]
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int m = m0 + 16 * (2 * w + mi) + i16;
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const int n = n0 + wn + 16 * nb + 4 * g;
-      if constexpr (MODE == GemmOut::Partial) {
-        float* dst = (float*)a.Y + ((long long)split * a.M + m) * a.N + n;
-        *(f32x4*)dst = acc[mi][nb];
-      } else {
-        bf16* dst = (bf16*)a.Y + (long long)m * a.N + n;
-        const bf16x4 o = {(bf16)acc[mi][nb][0], (bf16)acc[mi][nb][1], (bf16)acc[mi][nb][2], (bf16)acc[mi][nb][3]};
-        *(bf16x4*)dst = o;
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ bf16 weights
-// The product for bf16 weights. A workgroup of eight waves (two per SIMD)
+// ------------------------------------------------------------------ MFMA product
+// The product for bf16 and block-fp8 weights. A workgroup of eight waves (two per SIMD)
 // owns TN weight rows x 128 batch rows and one K range; each 64-wide K chunk
 // of both operands goes HBM -> LDS by direct-to-LDS DMA into a ring, every
 // wave issuing its share, one barrier per chunk. Wave w owns 16 WN weight rows
@@ -282,15 +67,18 @@ __global__ __launch_bounds__(NW * 2, 1) void gemm_bf16_kernel(GemmArgs a) {
 // weight bytes take to arrive, so the wave tile keeps LDS reads down
 // (each fragment feeds WM or WN MFMAs), two waves per SIMD fill each other's
 // gaps, and the second k-block's fragments are read while the first
-// k-block's MFMAs run. TN = 64 for products whose activations stay in L2, 128
-// (weights read nontemporal) for the out-projection.
-template <int TN, int WN, int WM>
+// k-block's MFMAs run. bf16 weights: TN = 64 for products whose activations
+// stay in L2, 128 (weights read nontemporal) for the out-projection.
+// Block-fp8 weights (W8, 64-byte rows per chunk): TN = 128, or 256 for the
+// out-projection, so a chunk stage holds about as many bytes as for bf16.
+template <int TN, int WN, int WM, bool W8 = false>
 struct PTile {
   static constexpr int kWaves = 8;
   static constexpr int kWavesN = TN / (16 * WN);
   static constexpr int kWavesM = 8 / WM;
   static_assert(kWavesN * kWavesM == kWaves, "wave grid");
-  static constexpr int kWBytes = TN * 128;                 // weight rows x 64 bf16
+  static constexpr int kWRow = W8 ? 64 : 128;              // bytes of a weight row per chunk (64 e4m3 / bf16)
+  static constexpr int kWBytes = TN * kWRow;
   static constexpr int kXBytes = kGM * 128;                // activation rows x 64 bf16
   static constexpr int kStageBytes = kWBytes + kXBytes;
   // three chunks in flight (measured on MI355X: five in flight for either width,
@@ -298,15 +86,16 @@ struct PTile {
   static constexpr int kStages = 4;
   static_assert(kStages * kStageBytes <= 160 * 1024, "LDS");
   static constexpr int kDpw = kStageBytes / 1024 / kWaves;  // 1 KB DMAs per wave per chunk
+  static_assert(kDpw * kWaves * 1024 == kStageBytes, "DMA blocks dealt evenly");
   static_assert((kStages - 1) * kDpw < 64, "DMAs in flight exceed the wait counter");
 };
 
 // lgkmcnt(0) only: this wave's LDS reads have completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-template <int TN, int WN, int WM>
+template <int TN, int WN, int WM, bool W8>
 __device__ __forceinline__ void pipe_issue(const GemmArgs& a, int n0, int m0, int kc, char* stage, int w, int lane) {
-  using T = PTile<TN, WN, WM>;
+  using T = PTile<TN, WN, WM, W8>;
   const int r_in = lane >> 3;  // 8 rows of 128 B per 1 KB block
   const int pc = lane & 7;
   const int k0 = kc * kGK;
@@ -314,7 +103,15 @@ __device__ __forceinline__ void pipe_issue(const GemmArgs& a, int n0, int m0, in
 #pragma unroll
   for (int jj = 0; jj < T::kDpw; ++jj) {
     const int blk = T::kDpw * w + jj;  // weight blocks first, then activation blocks
-    if (blk < kWBlocks) {
+    if (W8 && blk < kWBlocks) {
+      // 16 rows of 64 weight bytes per 1 KB block, chunks swizzled by gswz8
+      const int r = 16 * blk + (lane >> 2);
+      const int n = n0 + r;
+      const unsigned char* wrow = n < a.N0 ? (const unsigned char*)a.W0 + (long long)n * a.K
+                                            : (const unsigned char*)a.W1 + (long long)(n - a.N0) * a.K;
+      __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + ((lane & 3) ^ gswz8(r)) * 16),
+                                       (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
+    } else if (blk < kWBlocks) {
       const int r = 8 * blk + r_in;
       const int n = n0 + r;
       const bf16* wrow = n < a.N0   ? a.W0 + (long long)n * a.K
@@ -333,9 +130,17 @@ __device__ __forceinline__ void pipe_issue(const GemmArgs& a, int n0, int m0, in
   }
 }
 
-template <GemmOut MODE, int TN, int WN, int WM>
+// W8: block-fp8 weights (e4m3 bytes, one fp32 scale per 128 x 128 block). A
+// lane reads one whole 16-byte chunk of its weight row (16 k values) and feeds
+// its halves to the chunk's two MFMAs, the activation fragments taking the
+// same contraction order (16-byte chunk 2g + j of the activation row for MFMA
+// j); the bytes are widened to bf16 exactly, each chunk's product goes to a
+// zeroed fp32 tile and is added to the accumulators times the chunk's block
+// scale (a wave's weight rows lie in one block row, a 64-wide chunk in one
+// block column).
+template <GemmOut MODE, int TN, int WN, int WM, bool W8 = false>
 __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
-  using T = PTile<TN, WN, WM>;
+  using T = PTile<TN, WN, WM, W8>;
   __shared__ __attribute__((aligned(1024))) char ring[T::kStages * T::kStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform((int)(threadIdx.x >> 6));
@@ -356,25 +161,71 @@ __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
   for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 tmp[W8 ? WN : 1][W8 ? WM : 1];  // W8: one chunk's product before its scale
+  u32x4 raw8[W8 ? WN : 1];              // W8: the weight bytes of the chunk being multiplied
+  const float* srow = nullptr;          // W8: this wave's row of block scales
+  if constexpr (W8) {
+    const int nrow = n0 + wn;
+    srow = nrow < a.N0 ? a.S0 + (long long)(nrow >> 7) * (a.K >> 7)
+                       : a.S1 + (long long)((nrow - a.N0) >> 7) * (a.K >> 7);
+  }
 
   // fragments of k-block j (32 of the chunk's 64) of chunk t: lane (i16, g)
-  // holds elements 32j + 8g .. +7 of weight row 16nb + i16 / batch row 16mb + i16
+  // holds elements 32j + 8g .. +7 (W8: 16g + 8j .. +7) of weight row
+  // 16nb + i16 and of batch row 16mb + i16. W8: frags reads the batch rows
+  // only; the chunk's weight bytes are read once by read_w8 and widened to
+  // bf16 per k-block by widen, away from the reads, so that the LDS latency
+  // hides behind MFMAs.
   auto frags = [&](int t, int j, bf16x8 (&wa)[WN], bf16x8 (&xb)[WM]) {
     const char* st = ring + (t % T::kStages) * T::kStageBytes;
-    const char* ws = st + wn * 128;
+    const char* ws = st + wn * T::kWRow;
     const char* xs = st + T::kWBytes + wm * 128;
-    const int off = ((4 * j + g) ^ gswz(i16)) << 4;
+    const int off = (((W8 ? 2 * g + j : 4 * j + g)) ^ gswz(i16)) << 4;
+    if constexpr (!W8) {
 #pragma unroll
-    for (int nb = 0; nb < WN; ++nb) wa[nb] = lds_read_b128((const MFA_LDS bf16x8*)(ws + (16 * nb + i16) * 128 + off));
+      for (int nb = 0; nb < WN; ++nb) wa[nb] = lds_read_b128((const MFA_LDS bf16x8*)(ws + (16 * nb + i16) * 128 + off));
+    }
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb) xb[mb] = lds_read_b128((const MFA_LDS bf16x8*)(xs + (16 * mb + i16) * 128 + off));
   };
-  auto mfmas = [&](const bf16x8 (&wa)[WN], const bf16x8 (&xb)[WM]) {
+  auto read_w8 = [&](int t) {
+    const char* ws = ring + (t % T::kStages) * T::kStageBytes + wn * T::kWRow;
 #pragma unroll
-    for (int nb = 0; nb < WN; ++nb)
+    for (int nb = 0; nb < WN; ++nb) {
+      const int r = 16 * nb + i16;
+      raw8[nb] = lds_read_u128((const MFA_LDS u32x4*)(ws + r * 64 + ((g ^ gswz8(r)) << 4)));
+    }
+  };
+  auto widen = [&](int j, bf16x8 (&wa)[WN]) {
 #pragma unroll
-      for (int mb = 0; mb < WM; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nb], xb[mb], acc[nb][mb], 0, 0, 0);
+    for (int nb = 0; nb < WN; ++nb) {
+      fp8x4_to_bf16(raw8[nb][2 * j], wa[nb], 0);
+      fp8x4_to_bf16(raw8[nb][2 * j + 1], wa[nb], 4);
+    }
+  };
+  // j = 0 / 1: the chunk's first / second k-block (W8: into tmp, then scaled
+  // in by sc, the chunk's block scale)
+  auto mfmas = [&](float sc, int j, const bf16x8 (&wa)[WN], const bf16x8 (&xb)[WM]) {
+    if constexpr (W8) {
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < WM; ++mb)
+          tmp[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nb], xb[mb], j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                                                                  : tmp[nb][mb], 0, 0, 0);
+      if (j == 1) {
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < WM; ++mb) acc[nb][mb] += tmp[nb][mb] * sc;
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < WM; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nb], xb[mb], acc[nb][mb], 0, 0, 0);
+    }
   };
 
   // Every stage starts filled; afterwards chunk t + kStages goes into the
@@ -383,7 +234,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < T::kStages; ++s)
     if (issued < nloc) {
-      pipe_issue<TN, WN, WM>(a, n0, m0, c_begin + issued, ring + s * T::kStageBytes, wave, lane);
+      pipe_issue<TN, WN, WM, W8>(a, n0, m0, c_begin + issued, ring + s * T::kStageBytes, wave, lane);
       ++issued;
     }
   bf16x8 wa0[WN], xb0[WM], wa1[WN], xb1[WM];
@@ -393,16 +244,24 @@ __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
+    if constexpr (W8) read_w8(0);
     frags(0, 0, wa0, xb0);
+    if constexpr (W8) {
+      wait_lds();
+      widen(0, wa0);
+    }
   }
   // Explicit LDS waits at the loop head and tail keep the compiler's own
   // wait analysis exact across the back edge (otherwise it waits for every
   // read, including those meant to overlap the MFMAs).
   wait_lds();
   for (int t = 0; t + 1 < nloc; ++t) {
+    // W8: the scale's load is covered by the LDS wait after the first MFMAs
+    const float sc = W8 ? load_scalar(srow, (c_begin + t) >> 1) : 0.f;
     frags(t, 1, wa1, xb1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(wa0, xb0);
+    if constexpr (W8) widen(1, wa1);
+    mfmas(sc, 0, wa0, xb0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lds();  // done reading chunk t
     // chunk t + 1 has landed once at most the chunks after it are in flight
@@ -412,19 +271,24 @@ __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (issued < nloc) {
-      pipe_issue<TN, WN, WM>(a, n0, m0, c_begin + issued, ring + (issued % T::kStages) * T::kStageBytes, wave, lane);
+      pipe_issue<TN, WN, WM, W8>(a, n0, m0, c_begin + issued, ring + (issued % T::kStages) * T::kStageBytes, wave,
+                                 lane);
       ++issued;
     }
+    if constexpr (W8) read_w8(t + 1);
     frags(t + 1, 0, wa0, xb0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(wa1, xb1);
+    mfmas(sc, 1, wa1, xb1);
     __builtin_amdgcn_sched_barrier(0);
     wait_lds();
+    if constexpr (W8) widen(0, wa0);
   }
   if (nloc > 0) {
+    const float sc = W8 ? load_scalar(srow, (c_begin + nloc - 1) >> 1) : 0.f;
     frags(nloc - 1, 1, wa1, xb1);
-    mfmas(wa0, xb0);
-    mfmas(wa1, xb1);
+    if constexpr (W8) widen(1, wa1);
+    mfmas(sc, 0, wa0, xb0);
+    mfmas(sc, 1, wa1, xb1);
   }
 
   // lane (i16, g), register i of acc[nb][mb] = Y[m0 + wm + 16mb + i16][n0 + wn + 16nb + 4g + i]
@@ -708,11 +572,11 @@ hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const v
   const bool part = mode == GemmOut::Partial;
   if (p.w8) {
     if (p.tile_n == 256)
-      return part ? launch(gemm_bf16_kernel<GemmOut::Partial, 256, true>, grid, dim3(512), stream, a)
-                  : launch(gemm_bf16_kernel<GemmOut::Direct, 256, true>, grid, dim3(512), stream, a);
+      return part ? launch(gemm_pipe_kernel<GemmOut::Partial, 256, 4, 4, true>, grid, dim3(512), stream, a)
+                  : launch(gemm_pipe_kernel<GemmOut::Direct, 256, 4, 4, true>, grid, dim3(512), stream, a);
     if (p.tile_n == 128)
-      return part ? launch(gemm_bf16_kernel<GemmOut::Partial, 128, true>, grid, dim3(256), stream, a)
-                  : launch(gemm_bf16_kernel<GemmOut::Direct, 128, true>, grid, dim3(256), stream, a);
+      return part ? launch(gemm_pipe_kernel<GemmOut::Partial, 128, 4, 2, true>, grid, dim3(512), stream, a)
+                  : launch(gemm_pipe_kernel<GemmOut::Direct, 128, 4, 2, true>, grid, dim3(512), stream, a);
     return hipErrorInvalidValue;
   }
   if (p.tile_n == 64)
