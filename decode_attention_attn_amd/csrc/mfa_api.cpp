@@ -157,13 +157,13 @@ size_t mfa_qproj_kv_append_workspace_size(int B) {
   return mfa::qkv_layout(B).total;
 }
 
-int mfa_qproj_kv_append(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq,
-                        const void* w_k, const void* w_v, void* q_out, void* k_cache, void* v_cache,
-                        const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
-                        float v_scale, void* ws, size_t ws_bytes, int B, mfa_dtype cache_dt, void* stream) {
-  if (!x || !w_dq || !w_uq || !w_k || !w_v || !q_out || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 ||
-      B > MFA_MAX_BATCH || !(eps >= 0.f) || !isfinite(eps))
-    return MFA_ERR_INVALID_ARG;
+// The stacked product and its epilogue, then the q up-projection; s_* are the
+// block scales of block-fp8 weights (all null for bf16 weights).
+static int qkv_run(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps, const void* w_uq,
+                   const float* s_uq, const void* w_k, const float* s_k, const void* w_v, const float* s_v,
+                   void* q_out, void* k_cache, void* v_cache, const int64_t* seq_off, const int32_t* seq_len,
+                   int32_t* seq_len_out, float k_scale, float v_scale, void* ws, size_t ws_bytes, int B,
+                   mfa_dtype cache_dt, hipStream_t s) {
   if (cache_dt != MFA_BF16 && cache_dt != MFA_FP8_E4M3) return MFA_ERR_UNSUPPORTED;
   const bool fp8 = cache_dt == MFA_FP8_E4M3;
   float inv_k = 1.f, inv_v = 1.f;
@@ -177,33 +177,57 @@ int mfa_qproj_kv_append(const void* x, const void* w_dq, const float* gamma, flo
   }
   if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(w_k) || !aligned16(w_v) ||
       !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws) || !aligned_n(seq_off, 8) ||
-      !aligned_n(seq_len, 4) || !aligned_n(seq_len_out, 4) || (gamma && !aligned_n(gamma, 4)))
+      !aligned_n(seq_len, 4) || !aligned_n(seq_len_out, 4) || (gamma && !aligned_n(gamma, 4)) ||
+      (s_dq && (!aligned_n(s_dq, 4) || !aligned_n(s_uq, 4) || !aligned_n(s_k, 4) || !aligned_n(s_v, 4))))
     return MFA_ERR_ALIGNMENT;
   if (!ws || ws_bytes < mfa_qproj_kv_append_workspace_size(B)) return MFA_ERR_WORKSPACE;
   int st = MFA_OK;
   const int cus = plan_cus(&st);
   if (st != MFA_OK) return st;
-  const mfa::GemmPlan dn = mfa::plan_gemm(true, B, mfa::kPlanQkv, MFA_HIDDEN, MFA_RANK, cus);
-  const mfa::GemmPlan up = mfa::plan_gemm(true, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus);
+  const bool w8 = s_dq != nullptr;
+  const mfa::GemmPlan dn = mfa::plan_gemm(true, B, mfa::kPlanQkv, MFA_HIDDEN, MFA_RANK, cus, w8);
+  const mfa::GemmPlan up = mfa::plan_gemm(true, B, MFA_QDIM, MFA_RANK, MFA_QDIM, cus, w8);
   const mfa::QprojLayout l = mfa::qkv_layout(B);
   if (mfa::qproj_part_need(B, true, dn, up) > l.part_bytes) return MFA_ERR_WORKSPACE;  // a planning bug, never run
-  hipStream_t s = (hipStream_t)stream;
   float* part = (float*)ws;
   void* chat = (char*)ws + l.chat_offset;
   // rows 0..2047 of the product from W_dq, 2048..2303 from W_k, 2304..2559 from W_v
-  hipError_t e = mfa::launch_gemm(true, dn, x, w_dq, w_k, part, mfa::GemmOut::Partial, s, nullptr, nullptr, w_v,
-                                  MFA_RANK + MFA_HEAD_DIM);
+  hipError_t e = mfa::launch_gemm(true, dn, x, w_dq, w_k, part, mfa::GemmOut::Partial, s, s_dq, s_k, w_v,
+                                  MFA_RANK + MFA_HEAD_DIM, s_v);
   if (e != hipSuccess) return hip_status(e);
   e = mfa::launch_qkv_epilogue(part, dn.splits, B, gamma, eps, chat, k_cache, v_cache, seq_off, seq_len, fp8, inv_k,
                                inv_v, seq_len_out, s);
   if (e != hipSuccess) return hip_status(e);
   if (up.splits > 1) {
     // the first product's partials were consumed by the epilogue above
-    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s);
+    e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s, s_uq, s_uq);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s, up.w8 ? 0 : up.tile_n));
   }
-  return hip_status(mfa::launch_gemm(true, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s));
+  return hip_status(mfa::launch_gemm(true, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s, s_uq, s_uq));
+}
+
+int mfa_qproj_kv_append(const void* x, const void* w_dq, const float* gamma, float eps, const void* w_uq,
+                        const void* w_k, const void* w_v, void* q_out, void* k_cache, void* v_cache,
+                        const int64_t* seq_off, const int32_t* seq_len, int32_t* seq_len_out, float k_scale,
+                        float v_scale, void* ws, size_t ws_bytes, int B, mfa_dtype cache_dt, void* stream) {
+  if (!x || !w_dq || !w_uq || !w_k || !w_v || !q_out || !k_cache || !v_cache || !seq_off || !seq_len || B < 1 ||
+      B > MFA_MAX_BATCH || !(eps >= 0.f) || !isfinite(eps))
+    return MFA_ERR_INVALID_ARG;
+  return qkv_run(x, w_dq, nullptr, gamma, eps, w_uq, nullptr, w_k, nullptr, w_v, nullptr, q_out, k_cache, v_cache,
+                 seq_off, seq_len, seq_len_out, k_scale, v_scale, ws, ws_bytes, B, cache_dt, (hipStream_t)stream);
+}
+
+int mfa_qproj_kv_append_w8(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps,
+                           const void* w_uq, const float* s_uq, const void* w_k, const float* s_k, const void* w_v,
+                           const float* s_v, void* q_out, void* k_cache, void* v_cache, const int64_t* seq_off,
+                           const int32_t* seq_len, int32_t* seq_len_out, float k_scale, float v_scale, void* ws,
+                           size_t ws_bytes, int B, mfa_dtype cache_dt, void* stream) {
+  if (!x || !w_dq || !s_dq || !w_uq || !s_uq || !w_k || !s_k || !w_v || !s_v || !q_out || !k_cache || !v_cache ||
+      !seq_off || !seq_len || B < 1 || B > MFA_MAX_BATCH || !(eps >= 0.f) || !isfinite(eps))
+    return MFA_ERR_INVALID_ARG;
+  return qkv_run(x, w_dq, s_dq, gamma, eps, w_uq, s_uq, w_k, s_k, w_v, s_v, q_out, k_cache, v_cache, seq_off,
+                 seq_len, seq_len_out, k_scale, v_scale, ws, ws_bytes, B, cache_dt, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ K/V append

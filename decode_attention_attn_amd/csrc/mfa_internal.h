@@ -81,10 +81,11 @@ enum class GemmOut {
 };
 
 // S0 / S1 non-null: W0 / W1 are block-fp8 (e4m3 bytes, fp32 scales per 128 x 128 block, [rows/128][K/128])
-// W2 non-null (bf16 weights only): rows N0 <= n < N1 from W1, n >= N1 from W2.
+// W2 non-null (MFMA path): rows N0 <= n < N1 from W1, n >= N1 from W2; for block-fp8 weights S2 holds W2's
+// scales and N0, N1 are multiples of 128.
 hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
                        GemmOut mode, hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr,
-                       const void* W2 = nullptr, int N1 = 0);
+                       const void* W2 = nullptr, int N1 = 0, const float* S2 = nullptr);
 
 // c_hat[M, N] = rmsnorm(sum_s part[s]) * gamma, in the activation dtype.
 hipError_t launch_rmsnorm_reduce(bool bf16, const float* part, int S, int M, int N, const float* gamma,

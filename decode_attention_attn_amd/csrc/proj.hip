@@ -26,17 +26,18 @@ constexpr int kGM = kGemmTileM;  // batch rows per workgroup
 constexpr int kGK = kGemmChunkK; // K per stage
 
 // Weight rows n < N0 come from W0, N0 <= n < N1 from W1, n >= N1 from W2
-// (N1 = N: two matrices; bf16 weights only for a third one).
+// (N1 = N: two matrices), block-fp8 scales from S0, S1, S2 alike.
 struct GemmArgs {
   const bf16* X;
   const bf16* W0;  // (e4m3 bytes for block-fp8 weights)
   const bf16* W1;
   void* Y;
   int M, N, K, N0, S;
-  const float* S0;  // block-fp8: [rows / 128][K / 128] scales of W0 / W1
+  const float* S0;  // block-fp8: [rows / 128][K / 128] scales of W0 / W1 / W2
   const float* S1;
   const bf16* W2;
   int N1;
+  const float* S2;
 };
 
 // 16-byte chunk swizzle for the 64-byte rows of a block-fp8 weight chunk: a
@@ -107,8 +108,9 @@ __device__ __forceinline__ void pipe_issue(const GemmArgs& a, int n0, int m0, in
       // 16 rows of 64 weight bytes per 1 KB block, chunks swizzled by gswz8
       const int r = 16 * blk + (lane >> 2);
       const int n = n0 + r;
-      const unsigned char* wrow = n < a.N0 ? (const unsigned char*)a.W0 + (long long)n * a.K
-                                            : (const unsigned char*)a.W1 + (long long)(n - a.N0) * a.K;
+      const unsigned char* wrow = n < a.N0   ? (const unsigned char*)a.W0 + (long long)n * a.K
+                                  : n < a.N1 ? (const unsigned char*)a.W1 + (long long)(n - a.N0) * a.K
+                                             : (const unsigned char*)a.W2 + (long long)(n - a.N1) * a.K;
       __builtin_amdgcn_global_load_lds((const void*)(wrow + k0 + ((lane & 3) ^ gswz8(r)) * 16),
                                        (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
     } else if (blk < kWBlocks) {
@@ -166,8 +168,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
   const float* srow = nullptr;          // W8: this wave's row of block scales
   if constexpr (W8) {
     const int nrow = n0 + wn;
-    srow = nrow < a.N0 ? a.S0 + (long long)(nrow >> 7) * (a.K >> 7)
-                       : a.S1 + (long long)((nrow - a.N0) >> 7) * (a.K >> 7);
+    srow = nrow < a.N0   ? a.S0 + (long long)(nrow >> 7) * (a.K >> 7)
+           : nrow < a.N1 ? a.S1 + (long long)((nrow - a.N0) >> 7) * (a.K >> 7)
+                         : a.S2 + (long long)((nrow - a.N1) >> 7) * (a.K >> 7);
   }
 
   // fragments of k-block j (32 of the chunk's 64) of chunk t: lane (i16, g)
@@ -552,12 +555,17 @@ __global__ __launch_bounds__(512) void qkv_epilogue_kernel(const float* part, in
 
 // ------------------------------------------------------------------ host side
 hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const void* W0, const void* W1, void* Y,
-                       GemmOut mode, hipStream_t stream, const float* S0, const float* S1, const void* W2, int N1) {
+                       GemmOut mode, hipStream_t stream, const float* S0, const float* S1, const void* W2, int N1,
+                       const float* S2) {
   if (W2 == nullptr) {
     W2 = W1;
+    S2 = S1;
     N1 = p.N;
-  } else if (!bf16_path || S0 != nullptr) {
-    return hipErrorInvalidValue;  // a third matrix only for bf16 weights
+  } else if (!bf16_path || (S0 != nullptr) != (S2 != nullptr) || N1 < p.N0 || N1 > p.N ||
+             (S0 != nullptr && (p.N0 % 128 != 0 || N1 % 128 != 0))) {
+    // a third matrix only on the MFMA path; for block-fp8 weights with its
+    // scales, every matrix starting on a 128-row scale block
+    return hipErrorInvalidValue;
   }
   if (!bf16_path) {
     return launch(gemm_f32_kernel, dim3((p.N + 3) / 4), dim3(256), stream, (const float*)X, (const float*)W0,
@@ -567,7 +575,7 @@ hipError_t launch_gemm(bool bf16_path, const GemmPlan& p, const void* X, const v
   // tiles, bf16 plans 64/128-column tiles of the pipelined kernel
   if ((S0 != nullptr) != p.w8 || p.N % p.tile_n != 0) return hipErrorInvalidValue;
   GemmArgs a{(const bf16*)X, (const bf16*)W0, (const bf16*)W1, Y, p.M, p.N, p.K, p.N0, p.splits, S0, S1,
-             (const bf16*)W2, N1};
+             (const bf16*)W2, N1, S2};
   const dim3 grid(p.N / p.tile_n, p.splits, p.mchunks);
   const bool part = mode == GemmOut::Partial;
   if (p.w8) {

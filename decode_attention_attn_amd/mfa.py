@@ -83,6 +83,9 @@ _lib.mfa_kv_append_w8.restype = _I
 _lib.mfa_kv_append_w8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _F, _P, _Z, _I, _P]
 _lib.mfa_oproj_w8.restype = _I
 _lib.mfa_oproj_w8.argtypes = [_P, _P, _P, _P, _P, _Z, _I, _P]
+_lib.mfa_qproj_kv_append_w8.restype = _I
+_lib.mfa_qproj_kv_append_w8.argtypes = [_P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _F,
+                                        _P, _Z, _I, _I, _P]
 _lib.mfa_bw_probe.restype = _I
 _lib.mfa_bw_probe.argtypes = [_P, _Z, _P, _I, _P]
 _lib.mfa_oproj_workspace_size.restype = _Z
@@ -99,7 +102,7 @@ EXPORTED = [
     "mfa_decode_attn_paged_mt",
     "mfa_decode_attn_mt_workspace_size", "mfa_decode_attn_mt",
     "mfa_oproj_workspace_size", "mfa_oproj",
-    "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8", "mfa_bw_probe",
+    "mfa_qproj_w8", "mfa_kv_append_w8", "mfa_oproj_w8", "mfa_qproj_kv_append_w8", "mfa_bw_probe",
 ]
 
 
@@ -266,6 +269,15 @@ def mfa_kv_append_w8(x, w_k, s_k, w_v, s_v, k_cache, v_cache, seq_off, seq_len, 
 
 def mfa_oproj_w8(attn, w_o, s_o, y, ws, B, stream=None) -> int:
     return _lib.mfa_oproj_w8(_ptr(attn), _ptr(w_o), _ptr(s_o), _ptr(y), _ptr(ws), _nbytes(ws), B, _stream(stream))
+
+
+def mfa_qproj_kv_append_w8(x, w_dq, s_dq, gamma, eps, w_uq, s_uq, w_k, s_k, w_v, s_v, q_out, k_cache, v_cache,
+                           seq_off, seq_len, k_scale, v_scale, ws, B, cache_dt, stream=None, seq_len_out=None) -> int:
+    return _lib.mfa_qproj_kv_append_w8(_ptr(x), _ptr(w_dq), _ptr(s_dq), _ptr(gamma), eps, _ptr(w_uq), _ptr(s_uq),
+                                       _ptr(w_k), _ptr(s_k), _ptr(w_v), _ptr(s_v), _ptr(q_out), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(seq_off), _ptr(seq_len), _ptr(seq_len_out),
+                                       float(k_scale), float(v_scale), _ptr(ws), _nbytes(ws), B, cache_dt,
+                                       _stream(stream))
 
 
 def mfa_bw_probe(buf, sink, num_workgroups=0, stream=None) -> int:

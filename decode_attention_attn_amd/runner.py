@@ -168,10 +168,10 @@ class LayerCall:
         self.ws_kv = _ws(mfa.mfa_kv_append_workspace_size(B, dt), device)
         self.ws_a = _ws(mfa.mfa_decode_attn_workspace_size(B, num_workgroups), device)
         self.ws_o = _ws(mfa.mfa_oproj_workspace_size(B, dt), device)
-        # bf16 activations and weights: the q path and the K/V append as one call
-        # (one product over [W_dq; W_k; W_v], mfa_qproj_kv_append)
-        self.fused = (fused_q_kv and dev["kind_w"] != FP8_BLOCK and dev["kind_act"] == BF16
-                      and dev["kind_kv"] in (BF16, FP8))
+        # bf16 activations: the q path and the K/V append as one call (one
+        # product over [W_dq; W_k; W_v], mfa_qproj_kv_append, or
+        # mfa_qproj_kv_append_w8 for block-fp8 weights)
+        self.fused = fused_q_kv and dev["kind_act"] == BF16 and dev["kind_kv"] in (BF16, FP8)
         self.ws_qkv = _ws(mfa.mfa_qproj_kv_append_workspace_size(B), device) if self.fused else None
 
     def __call__(self):
@@ -209,15 +209,23 @@ class LayerCall:
                                         B, dt, _DT[d["kind_kv"]], s, seq_len_out=self.len_after), "mfa_kv_append")
 
     def _call_w8(self):
-        # block-fp8 weights: the same four steps through the _w8 entry points
+        # block-fp8 weights: the same steps through the _w8 entry points
         # (bf16 activations; the cache is bf16 or e4m3)
         d, dt, s = self.dev, self.dt, self.stream
         B = d["B"]
-        mfa.check(mfa.mfa_qproj_w8(d["x"], d["w_dq"], d["w_dq_scale"], None, d["eps"], d["w_uq"], d["w_uq_scale"],
-                                   self.q, self.ws_q, B, s), "mfa_qproj_w8")
-        mfa.check(mfa.mfa_kv_append_w8(d["x"], d["w_k"], d["w_k_scale"], d["w_v"], d["w_v_scale"], d["k"], d["v"],
-                                       d["off"], d["len"], _DT[d["kind_kv"]], d["k_scale"], d["v_scale"],
-                                       self.ws_kv, B, s, seq_len_out=self.len_after), "mfa_kv_append_w8")
+        if self.fused:
+            mfa.check(mfa.mfa_qproj_kv_append_w8(d["x"], d["w_dq"], d["w_dq_scale"], None, d["eps"], d["w_uq"],
+                                                 d["w_uq_scale"], d["w_k"], d["w_k_scale"], d["w_v"], d["w_v_scale"],
+                                                 self.q, d["k"], d["v"], d["off"], d["len"], d["k_scale"],
+                                                 d["v_scale"], self.ws_qkv, B, _DT[d["kind_kv"]], s,
+                                                 seq_len_out=self.len_after), "mfa_qproj_kv_append_w8")
+        else:
+            mfa.check(mfa.mfa_qproj_w8(d["x"], d["w_dq"], d["w_dq_scale"], None, d["eps"], d["w_uq"],
+                                       d["w_uq_scale"], self.q, self.ws_q, B, s), "mfa_qproj_w8")
+            mfa.check(mfa.mfa_kv_append_w8(d["x"], d["w_k"], d["w_k_scale"], d["w_v"], d["w_v_scale"], d["k"],
+                                           d["v"], d["off"], d["len"], _DT[d["kind_kv"]], d["k_scale"],
+                                           d["v_scale"], self.ws_kv, B, s, seq_len_out=self.len_after),
+                      "mfa_kv_append_w8")
         mfa.check(mfa.mfa_decode_attn(self.q, d["k"], d["v"], d["off"], self.len_after, SOFTMAX_SCALE,
                                       d["k_scale"], d["v_scale"], self.o, self.lse, self.ws_a, B, self.G, dt,
                                       _DT[d["kind_kv"]], s),

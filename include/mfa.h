@@ -272,7 +272,10 @@ int mfa_oproj(const void* attn, const void* w_o, void* y, void* ws, size_t ws_by
  * those of the bf16 calls (mfa_qproj_workspace_size(B, MFA_BF16), ...).
  * mfa_kv_append_w8 writes a bf16 cache (cache_dt = MFA_BF16, scales unused)
  * or an e4m3 cache as mfa_kv_append_fp8 does (cache_dt = MFA_FP8_E4M3);
- * seq_len_out as for mfa_kv_append.
+ * seq_len_out as for mfa_kv_append. mfa_qproj_kv_append_w8 is
+ * mfa_qproj_kv_append with these weights (one product over the stacked
+ * [W_dq; W_k; W_v] bytes, each matrix with its own scales; the same
+ * workspace, mfa_qproj_kv_append_workspace_size(B), and cache_dt choices).
  * Scale arrays: device fp32, 4-byte aligned.
  */
 int mfa_qproj_w8(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps,
@@ -284,6 +287,11 @@ int mfa_kv_append_w8(const void* x, const void* w_k, const float* s_k, const voi
                      size_t ws_bytes, int B, void* stream);
 int mfa_oproj_w8(const void* attn, const void* w_o, const float* s_o, void* y, void* ws, size_t ws_bytes,
                  int B, void* stream);
+int mfa_qproj_kv_append_w8(const void* x, const void* w_dq, const float* s_dq, const float* gamma, float eps,
+                           const void* w_uq, const float* s_uq, const void* w_k, const float* s_k, const void* w_v,
+                           const float* s_v, void* q_out, void* k_cache, void* v_cache, const int64_t* seq_off,
+                           const int32_t* seq_len, int32_t* seq_len_out, float k_scale, float v_scale, void* ws,
+                           size_t ws_bytes, int B, mfa_dtype cache_dt, void* stream);
 
 /* ------------------------------------------------------------------ bandwidth probe
  * Measures the achievable HBM read rate that the attention kernels' KV rate

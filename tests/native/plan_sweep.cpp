@@ -54,22 +54,27 @@ int main() {
           checked += 3;
         }
     }
-    // the q path with the K/V projections folded in (bf16 only)
+    // the q path with the K/V projections folded in (bf16 activations, either weight format)
     const QprojLayout qk = qkv_layout(B);
     if (qk.chat_offset < qk.part_bytes || qk.total < qk.chat_offset + (size_t)B * kPlanRank * 2) {
       printf("qkv layout overlaps: B=%d\n", B);
       ++bad;
     }
-    for (int cus = 1; cus <= kPlanCus; ++cus) {
-      const GemmPlan dn = plan_gemm(true, B, kPlanQkv, kPlanHidden, kPlanRank, cus);
-      const GemmPlan up = plan_gemm(true, B, kPlanQDim, kPlanRank, kPlanQDim, cus);
-      const size_t need = qproj_part_need(B, true, dn, up);
-      if (need > qk.part_bytes) {
-        printf("qkv: B=%d cus=%d needs %zu > %zu\n", B, cus, need, qk.part_bytes);
-        ++bad;
+    for (int w8 = 0; w8 < 2; ++w8)
+      for (int cus = 1; cus <= kPlanCus; ++cus) {
+        const GemmPlan dn = plan_gemm(true, B, kPlanQkv, kPlanHidden, kPlanRank, cus, w8);
+        const GemmPlan up = plan_gemm(true, B, kPlanQDim, kPlanRank, kPlanQDim, cus, w8);
+        const size_t need = qproj_part_need(B, true, dn, up);
+        if (need > qk.part_bytes) {
+          printf("qkv: B=%d w8=%d cus=%d needs %zu > %zu\n", B, w8, cus, need, qk.part_bytes);
+          ++bad;
+        }
+        if (dn.N % dn.tile_n != 0 || up.N % up.tile_n != 0) {
+          printf("qkv tile: B=%d w8=%d cus=%d tiles %d / %d\n", B, w8, cus, dn.tile_n, up.tile_n);
+          ++bad;
+        }
+        ++checked;
       }
-      ++checked;
-    }
   }
   printf("checked %ld plans, %ld over their workspace\n", checked, bad);
   return bad == 0 ? 0 : 1;

@@ -269,6 +269,38 @@ def test_block_fp8_projections_reject_bad_arguments():
         assert op(FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 128, None) == mfa.MFA_ERR_WORKSPACE
 
 
+def test_block_fp8_qproj_kv_append_rejects_bad_arguments():
+    f = mfa.raw_function("mfa_qproj_kv_append_w8")
+
+    def call(**kw):
+        a = dict(x=FAKE, wdq=FAKE, sdq=FAKE, gamma=None, eps=1e-6, wuq=FAKE, suq=FAKE, wk=FAKE, sk=FAKE, wv=FAKE,
+                 sv=FAKE, q=FAKE, kc=FAKE, vc=FAKE, off=FAKE, len=FAKE, lout=None, ks=1.0, vs=1.0, ws=FAKE,
+                 nbytes=1 << 40, B=4, cdt=mfa.MFA_FP8_E4M3)
+        a.update(kw)
+        return f(a["x"], a["wdq"], a["sdq"], a["gamma"], a["eps"], a["wuq"], a["suq"], a["wk"], a["sk"], a["wv"],
+                 a["sv"], a["q"], a["kc"], a["vc"], a["off"], a["len"], a["lout"], a["ks"], a["vs"], a["ws"],
+                 a["nbytes"], a["B"], a["cdt"], None)
+
+    need = mfa.mfa_qproj_kv_append_workspace_size(4)
+    for k in ("x", "wdq", "sdq", "wuq", "suq", "wk", "sk", "wv", "sv", "q", "kc", "vc", "off", "len"):
+        assert call(**{k: None}) == mfa.MFA_ERR_INVALID_ARG, k
+    assert call(B=0) == mfa.MFA_ERR_INVALID_ARG
+    assert call(B=mfa.MFA_MAX_BATCH + 1) == mfa.MFA_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == mfa.MFA_ERR_INVALID_ARG
+    assert call(cdt=mfa.MFA_F32) == mfa.MFA_ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-45):
+        assert call(ks=bad) == mfa.MFA_ERR_INVALID_ARG, bad
+        assert call(vs=bad) == mfa.MFA_ERR_INVALID_ARG, bad
+    # a bf16 cache ignores the cache scales
+    assert call(cdt=mfa.MFA_BF16, ks=0.0, nbytes=need - 1) == mfa.MFA_ERR_WORKSPACE
+    for k in ("sdq", "suq", "sk", "sv"):
+        assert call(**{k: FAKE + 2}) == mfa.MFA_ERR_ALIGNMENT, k
+    assert call(wk=MIS) == mfa.MFA_ERR_ALIGNMENT
+    assert call(lout=FAKE + 2) == mfa.MFA_ERR_ALIGNMENT
+    assert call(ws=None) == mfa.MFA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == mfa.MFA_ERR_WORKSPACE
+
+
 def test_bw_probe_rejects_bad_arguments():
     f = mfa.raw_function("mfa_bw_probe")
     assert f(None, 1024, FAKE, 8, None) == mfa.MFA_ERR_INVALID_ARG

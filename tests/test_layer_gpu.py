@@ -206,27 +206,38 @@ def test_layer_fp8_cache_small(G):
     _check_layer_fp8(gen.make_layer(w), num_workgroups=G)
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
-def test_layer_separate_q_and_kv_calls(cache):
-    # the layer step with mfa_qproj and mfa_kv_append(_fp8) as two calls (the
-    # default step makes them one mfa_qproj_kv_append call)
-    print(f"[case] layer B=5 ctx=300, {cache} cache, q path and K/V append as separate calls", flush=True)
+def _layer_workload(cache, w8, batch, ctx):
+    # bf16 or block-fp8 weights over a bf16 or e4m3 cache
+    if w8:
+        kv = gen.BF16 if cache == "bf16" else gen.FP8
+        return dataclasses.replace(gen.scaled(gen.WORKLOADS["layer_fp8_8k"], batch=batch, ctx=ctx), kv=kv)
     name = "layer_bf16_8k" if cache == "bf16" else "layer_bf16_fp8kv_8k"
-    inp = gen.make_layer(gen.scaled(gen.WORKLOADS[name], batch=5, ctx=300))
+    return gen.scaled(gen.WORKLOADS[name], batch=batch, ctx=ctx)
+
+
+@pytest.mark.parametrize("w8", [False, True])
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+def test_layer_separate_q_and_kv_calls(cache, w8):
+    # the layer step with mfa_qproj(_w8) and mfa_kv_append(_fp8/_w8) as two
+    # calls (the default step makes them one mfa_qproj_kv_append(_w8) call)
+    print(f"[case] layer B=5 ctx=300, {cache} cache, w8={w8}, q path and K/V append as separate calls", flush=True)
+    inp = gen.make_layer(_layer_workload(cache, w8, 5, 300))
     if cache == "bf16":
         _check_layer(inp, "bf16", fused=False)
     else:
         _check_layer_fp8(inp, fused=False)
 
 
+@pytest.mark.parametrize("w8", [False, True])
 @pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("B", [3, 200])
-def test_fused_q_kv_call_matches_the_separate_calls(cache, B):
+def test_fused_q_kv_call_matches_the_separate_calls(cache, B, w8):
     # the one-call q path + append against the two calls on the same inputs:
     # q, the appended rows and the lengths agree to fp32 summation order
-    print(f"[case] mfa_qproj_kv_append vs mfa_qproj + append, {cache} cache, B={B}", flush=True)
-    name = "layer_bf16_8k" if cache == "bf16" else "layer_bf16_fp8kv_8k"
-    inp = gen.make_layer(gen.scaled(gen.WORKLOADS[name], batch=B, ctx=40))
+    # (block-fp8 weights: mfa_qproj_kv_append_w8 against mfa_qproj_w8 +
+    # mfa_kv_append_w8)
+    print(f"[case] mfa_qproj_kv_append vs mfa_qproj + append, {cache} cache, B={B}, w8={w8}", flush=True)
+    inp = gen.make_layer(_layer_workload(cache, w8, B, 40))
     _, dev_f, call_f, _, _ = _run_layer(inp, fused=True)
     runner, dev_s, call_s, _, _ = _run_layer(inp, fused=False)
     assert call_f.fused and not call_s.fused
