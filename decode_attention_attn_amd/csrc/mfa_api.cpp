@@ -120,7 +120,7 @@ static int qproj_run(const void* x, const void* w_dq, const float* s_dq, const f
     // the down-projection's partials were consumed by the reduce above
     e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s, s_uq, s_uq);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s, up.w8 ? 0 : up.tile_n));
+    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s, up.tile_n));
   }
   return hip_status(mfa::launch_gemm(bf, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s, s_uq, s_uq));
 }
@@ -202,7 +202,7 @@ static int qkv_run(const void* x, const void* w_dq, const float* s_dq, const flo
     // the first product's partials were consumed by the epilogue above
     e = mfa::launch_gemm(true, up, chat, w_uq, w_uq, part, mfa::GemmOut::Partial, s, s_uq, s_uq);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s, up.w8 ? 0 : up.tile_n));
+    return hip_status(mfa::launch_sum_reduce(true, part, up.splits, B, MFA_QDIM, q_out, s, up.tile_n));
   }
   return hip_status(mfa::launch_gemm(true, up, chat, w_uq, w_uq, q_out, mfa::GemmOut::Direct, s, s_uq, s_uq));
 }
@@ -489,7 +489,7 @@ static int oproj_run(const void* attn, const void* w_o, const float* s_o, void* 
     hipError_t e = mfa::launch_gemm(true, plan, attn, w_o, w_o, ws, mfa::GemmOut::Partial, s, s_o, s_o);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(mfa::launch_sum_reduce(true, (const float*)ws, plan.splits, B, MFA_HIDDEN, y, s,
-                                             plan.w8 ? 0 : plan.tile_n));
+                                             plan.tile_n));
   }
   return hip_status(mfa::launch_gemm(bf, plan, attn, w_o, w_o, y, mfa::GemmOut::Direct, s, s_o, s_o));
 }

@@ -91,7 +91,8 @@ hipError_t launch_gemm(bool bf16, const GemmPlan& p, const void* X, const void* 
 hipError_t launch_rmsnorm_reduce(bool bf16, const float* part, int S, int M, int N, const float* gamma,
                                  float eps, void* out, hipStream_t stream);
 // out[M, N] = sum_s part[s], in the activation dtype. tile_n: the column tile of
-// the bf16-weight product that wrote the parts (its sum is then placed by tile), or 0.
+// the MFMA product that wrote the parts (its sum is then placed by tile where the
+// tile count is a multiple of 8 and the width 64 or 128), or 0.
 hipError_t launch_sum_reduce(bool bf16, const float* part, int S, int M, int N, void* out, hipStream_t stream,
                              int tile_n = 0);
 // rows m: k = sum_s part[s][m][0:256], v = sum_s part[s][m][256:512] written at cache row off[m] + len[m].
