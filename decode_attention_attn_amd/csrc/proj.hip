@@ -57,6 +57,17 @@ __device__ __forceinline__ u32x4 lds_read_u128(const MFA_LDS u32x4* __restrict__
 // cycles per read).
 __device__ __forceinline__ int gswz(int r) { return r & 7; }
 
+// Activation chunks under block-fp8 weights. There k-block j of a lane in
+// k-slot group g takes 16-byte chunk 2g + j of the activation row (the order
+// of the weight bytes), where bf16 weights take chunk 4j + g; read at the
+// same swizzle, that order cost 4 conflict cycles per read (measured). So
+// chunk c is stored where bf16 keeps chunk ((c & 1) << 2) | (c >> 1) (its
+// three bits rotated, 2g + j -> 4j + g), and the block-fp8 activation reads
+// use the very addresses of the bf16 ones. act8_chunk is the inverse
+// rotation: LDS chunk slot p of a row (before the swizzle) holds activation
+// chunk act8_chunk(p).
+__device__ __forceinline__ int act8_chunk(int p) { return ((p & 3) << 1) | (p >> 2); }
+
 // ------------------------------------------------------------------ MFMA product
 // The product for bf16 and block-fp8 weights. A workgroup of eight waves (two per SIMD)
 // owns TN weight rows x 128 batch rows and one K range; each 64-wide K chunk
@@ -126,7 +137,8 @@ __device__ __forceinline__ void pipe_issue(const GemmArgs& a, int n0, int m0, in
       const int r = 8 * (blk - kWBlocks) + r_in;
       int m = m0 + r;
       m = m < a.M ? m : a.M - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(a.X + (long long)m * a.K + k0 + (pc ^ gswz(r)) * 8),
+      const int c = W8 ? act8_chunk(pc ^ gswz(r)) : pc ^ gswz(r);  // the chunk LDS slot pc of row r holds
+      __builtin_amdgcn_global_load_lds((const void*)(a.X + (long long)m * a.K + k0 + c * 8),
                                        (MFA_LDS void*)(stage + blk * 1024), 16, 0, 0);
     }
   }
@@ -183,7 +195,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pipe_kernel(GemmArgs a) {
     const char* st = ring + (t % T::kStages) * T::kStageBytes;
     const char* ws = st + wn * T::kWRow;
     const char* xs = st + T::kWBytes + wm * 128;
-    const int off = (((W8 ? 2 * g + j : 4 * j + g)) ^ gswz(i16)) << 4;
+    // (W8: activation chunk 2g + j, which the DMA stored in slot 4j + g)
+    const int off = ((4 * j + g) ^ gswz(i16)) << 4;
     if constexpr (!W8) {
 #pragma unroll
       for (int nb = 0; nb < WN; ++nb) wa[nb] = lds_read_b128((const MFA_LDS bf16x8*)(ws + (16 * nb + i16) * 128 + off));
