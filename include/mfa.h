@@ -53,8 +53,12 @@ extern "C" {
 
 /* Storage types. MFA_BF16 is bfloat16; MFA_FP8_E4M3 is the OCP 8-bit E4M3
  * ("fn": max 448, no infinity) with one fp32 scale per tensor (value = byte
- * value * scale). */
-typedef enum { MFA_F32 = 0, MFA_BF16 = 1, MFA_FP8_E4M3 = 2 } mfa_dtype;
+ * value * scale). mfa_dtype is a plain int, so that every value a caller may
+ * pass is well defined on both sides of the ABI (an enum type would give C++
+ * code undefined behaviour for values outside its enumerators); values other
+ * than these three are rejected with MFA_ERR_UNSUPPORTED. */
+enum { MFA_F32 = 0, MFA_BF16 = 1, MFA_FP8_E4M3 = 2 };
+typedef int mfa_dtype;
 
 enum {
   MFA_OK = 0,
